@@ -1,0 +1,206 @@
+"""Fused attention-KL primitive for MI355X: thin Python binding over libstreamkl.so.
+
+The library (csrc/streamkl.hip, C ABI in include/streamkl.h) computes, per
+query row, the forward KL divergence between the teacher and the student
+attention distributions, teacher first, in nats, without materialising either
+N_Q x N_K matrix, and the gradients of sum_r g_r KL_r with respect to the
+student queries and keys ("StreamKL: Fast and Memory-Efficient KL Divergence
+for Boosting Attention Distillation", abstract; direction and units: "Lecture
+05 - Where It All Lands", section 3.1).
+
+This module only marshals arguments: it checks tensor placement, dtype and
+shape, allocates the outputs with torch (device memory), and passes raw device
+pointers and torch's current HIP stream to the C entry points of the same
+names.  Every step of the computation runs in the HIP kernels; there is no
+fallback.  If the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstreamkl.so")
+
+STREAMKL_OK, STREAMKL_ERR_INVALID, STREAMKL_ERR_UNSUPPORTED, STREAMKL_ERR_WORKSPACE, STREAMKL_ERR_HIP = range(5)
+STREAMKL_F32, STREAMKL_BF16 = 0, 1
+
+_lib = None
+
+
+class StreamKLError(RuntimeError):
+    def __init__(self, where: str, code: int, text: str):
+        super().__init__(f"{where} failed: status {code} ({text})")
+        self.code = code
+
+
+def load_library():
+    """Load libstreamkl.so and declare its C signatures (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m attention_kl_divergence_amd.build "
+                           f"or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_int64)
+    lib.streamkl_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, vp, vp, vp, vp, vp]
+    lib.streamkl_fwd.restype = i
+    lib.streamkl_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, vp, vp, vp, f, vp, vp, vp]
+    lib.streamkl_bwd.restype = i
+    lib.streamkl_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.streamkl_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.streamkl_status_string.argtypes = [i]
+    lib.streamkl_status_string.restype = ctypes.c_char_p
+    lib.streamkl_supported.argtypes = [i, i, i]
+    lib.streamkl_supported.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().streamkl_status_string(int(code)).decode()
+
+
+def supported(dtype_code: int, d_t: int, d_s: int) -> bool:
+    return bool(load_library().streamkl_supported(int(dtype_code), int(d_t), int(d_s)))
+
+
+def _check(where, code):
+    if code != STREAMKL_OK:
+        raise StreamKLError(where, code, status_string(code))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return STREAMKL_BF16
+    if t.dtype == torch.float32:
+        return STREAMKL_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _inputs(q_t, k_t, q_s, k_s):
+    import torch
+    ts = (q_t, k_t, q_s, k_s)
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError("q_t, k_t, q_s, k_s must be 4-D tensors [B, H, N, d]")
+        if t.device.type != "cuda":
+            raise ValueError("inputs must be device (HIP) tensors")
+        if t.stride(-1) != 1:
+            raise ValueError("the last dimension must be contiguous")
+    if len({t.dtype for t in ts}) != 1 or len({t.device for t in ts}) != 1:
+        raise ValueError("inputs must share dtype and device")
+    B, H, n_q, d_t = q_t.shape
+    n_k = k_t.shape[2]
+    d_s = q_s.shape[3]
+    if tuple(k_t.shape) != (B, H, n_k, d_t) or tuple(q_s.shape) != (B, H, n_q, d_s) or \
+            tuple(k_s.shape) != (B, H, n_k, d_s):
+        raise ValueError("inconsistent shapes: q_t [B,H,Nq,dt], k_t [B,H,Nk,dt], q_s [B,H,Nq,ds], k_s [B,H,Nk,ds]")
+    strides = (ctypes.c_int64 * 12)(*[s for t in ts for s in (t.stride(0), t.stride(1), t.stride(2))])
+    return (B, H, n_q, n_k, d_t, d_s), strides
+
+
+def _stream_ptr(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _taus(tau_t, tau_s, d_t, d_s):
+    return (float(1.0 / math.sqrt(d_t)) if tau_t is None else float(tau_t),
+            float(1.0 / math.sqrt(d_s)) if tau_s is None else float(tau_s))
+
+
+def streamkl_fwd(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, with_sum=True):
+    """Forward: returns (kl_rows, lse_t, lse_s, kl_sum), fp32 device tensors.
+
+    kl_rows/lse_t/lse_s are [B, H, N_Q]; kl_sum is a 1-element tensor (None if
+    with_sum is False).  tau defaults to 1/sqrt(d) per side.
+    """
+    import torch
+    lib = load_library()
+    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
+    dev = q_t.device
+    kl = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
+    lt = torch.empty_like(kl)
+    ls = torch.empty_like(kl)
+    tot = torch.empty((1,), dtype=torch.float32, device=dev) if with_sum else None
+    code = lib.streamkl_fwd(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
+                            B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, int(bool(causal)),
+                            kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
+                            tot.data_ptr() if tot is not None else None, _stream_ptr(dev))
+    _check("streamkl_fwd", code)
+    return kl, lt, ls, tot
+
+
+def streamkl_bwd(q_t, k_t, q_s, k_s, lse_t, lse_s, grad_rows=None, grad_scalar=1.0,
+                 tau_t=None, tau_s=None, causal=False):
+    """Backward: returns (dq_s, dk_s) in the input dtype for L = sum_r g_r KL_r.
+
+    grad_rows: fp32 [B, H, N_Q] device tensor of dL/dKL_r, or None to use
+    grad_scalar for every row.
+    """
+    import torch
+    lib = load_library()
+    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
+    dev = q_t.device
+    for name, t in (("lse_t", lse_t), ("lse_s", lse_s)) + ((("grad_rows", grad_rows),) if grad_rows is not None else ()):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, n_q) or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous fp32 [B, H, N_Q] tensor on the inputs' device")
+    dq = torch.empty((B, H, n_q, d_s), dtype=q_s.dtype, device=dev)
+    dk = torch.empty((B, H, n_k, d_s), dtype=q_s.dtype, device=dev)
+    code = lib.streamkl_bwd(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
+                            B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, int(bool(causal)),
+                            lse_t.data_ptr(), lse_s.data_ptr(),
+                            grad_rows.data_ptr() if grad_rows is not None else None, float(grad_scalar),
+                            dq.data_ptr(), dk.data_ptr(), _stream_ptr(dev))
+    _check("streamkl_bwd", code)
+    return dq, dk
+
+
+def _autograd_function():
+    import torch
+
+    class StreamKLFunction(torch.autograd.Function):
+        """Per-row attention KL with gradients for the student queries and keys.
+
+        forward(q_t, k_t, q_s, k_s, tau_t, tau_s, causal) -> kl_rows [B, H, N_Q]
+        The teacher is a fixed target: q_t and k_t get no gradient.
+        """
+
+        @staticmethod
+        def forward(ctx, q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
+            kl, lt, ls, _ = streamkl_fwd(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, with_sum=False)
+            ctx.save_for_backward(q_t, k_t, q_s, k_s, lt, ls)
+            ctx.cfg = (tau_t, tau_s, causal)
+            return kl
+
+        @staticmethod
+        def backward(ctx, g):
+            q_t, k_t, q_s, k_s, lt, ls = ctx.saved_tensors
+            tau_t, tau_s, causal = ctx.cfg
+            g = g.to(torch.float32).contiguous()
+            dq, dk = streamkl_bwd(q_t, k_t, q_s, k_s, lt, ls, grad_rows=g,
+                                  tau_t=tau_t, tau_s=tau_s, causal=causal)
+            return None, None, dq, dk, None, None, None
+
+    return StreamKLFunction
+
+
+_fn_cache = None
+
+
+def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
+    """Differentiable per-row attention KL [B, H, N_Q] (gradients flow to q_s and k_s)."""
+    global _fn_cache
+    if _fn_cache is None:
+        _fn_cache = _autograd_function()
+    return _fn_cache.apply(q_t, k_t, q_s, k_s, tau_t, tau_s, causal)
+
+
+__all__ = ["streamkl_fwd", "streamkl_bwd", "attention_kl", "load_library", "supported", "status_string",
+           "StreamKLError", "STREAMKL_F32", "STREAMKL_BF16"]

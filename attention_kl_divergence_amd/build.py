@@ -1,0 +1,38 @@
+"""Compile the HIP library (gfx950 only) into attention_kl_divergence_amd/libstreamkl.so.
+
+One translation unit, csrc/streamkl.hip, built with hipcc for --offload-arch=gfx950.
+Packed fp32 VALU instructions are disabled for the device code (the host pass
+warns that it does not know the feature; that warning is harmless).
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "streamkl.hip")
+LIB = os.path.join(HERE, "libstreamkl.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    cmd = [HIPCC, *FLAGS, *extra, "-o", LIB + ".tmp", SRC]
+    if verbose:
+        print(" ".join(cmd))
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

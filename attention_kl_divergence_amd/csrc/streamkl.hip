@@ -1,0 +1,726 @@
+// Fused attention-KL forward and backward for MI355X (gfx950, CDNA4), behind the
+// C ABI declared in include/streamkl.h.
+//
+// Method: "StreamKL: Fast and Memory-Efficient KL Divergence for Boosting
+// Attention Distillation" (abstract) -- the KL between a teacher and a student
+// attention row is reduced in one streaming pass over key tiles with online
+// per-row state, and the backward recomputes both probability tiles from saved
+// per-row log-normalisers instead of storing any N_Q x N_K intermediate.  The
+// online normaliser is the running (max, sum) recurrence of "Online normalizer
+// calculation for softmax" (listed among the works the StreamKL page builds on).
+// The direction (teacher first) and nats follow "Lecture 05 - Where It All
+// Lands", section 3.1.
+//
+// gfx950 mapping (all tiles are 32x32, wave64):
+//  * Score tiles are produced transposed, C[y][x] = Y . X^T with
+//    v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x2_f32 for fp32 inputs): the
+//    "stationary" operand X (queries in the forward) sits in registers for the
+//    whole kernel, the "streamed" operand Y (keys in the forward) is staged
+//    through LDS, double-buffered, 16-byte coalesced loads.  In the accumulator
+//    layout lane l owns column x = l % 32 and 16 rows y, so every lane keeps the
+//    online state of ONE query over its own subset of keys with no cross-lane
+//    traffic in the hot loop; the two half-waves are merged once at the end with
+//    the associative merge of (max, normaliser, accumulators).
+//  * The contraction index d is split so that half-wave h owns the contiguous
+//    range [h*D/2, (h+1)*D/2): every operand load is a run of 16-byte vectors.
+//  * Backward gradients G^T[d][x] += Y_s^T[d][y] . dS[y][x]: dS is used straight
+//    from the accumulator registers as the B operand (the accumulator row
+//    order is taken as the contraction order), and the matching transposed
+//    student tile is read from the natural row-major LDS tile with
+//    ds_read_b64_tr_b16, so no transposed copy is ever written.
+//  * Workgroups are renumbered so that the blocks of one (batch, head) land on
+//    the same XCD (the hardware deals workgroups round-robin over the 8 XCDs,
+//    each with its own L2); causal blocks are issued heaviest first.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "streamkl.h"
+
+namespace {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Stand-in score for a masked key: finite, so that 0 * score stays 0 and the
+// running max of a lane that has seen no allowed key yet stays finite.
+constexpr float kMasked = -1.0e30f;
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kWaves = 4;
+constexpr int kTile = 32;      // MFMA tile edge; each wave owns 32 stationary items
+constexpr int kBlockX = kWaves * kTile;
+constexpr int kBN = 32;        // streamed rows per pipeline stage
+
+// ---------------------------------------------------------------- type traits
+template <typename T> struct Ty;
+template <> struct Ty<bf16_t> {
+    static constexpr int kBytes = 2;
+    using Frag = bf16x8;
+    __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    // k-step ks of a half-wave span held as 16-byte vectors: 8 bf16 per step
+    __device__ static inline Frag frag(const u32x4 *v, int ks) { return __builtin_bit_cast(Frag, v[ks]); }
+    static constexpr int ksteps(int D) { return D / 16; }
+};
+template <> struct Ty<float> {
+    static constexpr int kBytes = 4;
+    using Frag = float;
+    __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline Frag frag(const u32x4 *v, int ks) {
+        // take the element as a scalar first: a bit_cast applied to a vector
+        // element expression reads element 0 with this compiler
+        const unsigned u = v[ks >> 2][ks & 3];
+        return __builtin_bit_cast(float, u);
+    }
+    static constexpr int ksteps(int D) { return D / 2; }
+};
+
+// 16-byte vectors in one half-wave span of a D-wide row
+template <typename T, int D> constexpr int span_vecs() { return D * Ty<T>::kBytes / 32; }
+// LDS row pitch: 16 bytes of padding keep the 32 rows of a 16-byte column read
+// on distinct banks
+template <typename T, int D> constexpr int lds_pitch() { return D * Ty<T>::kBytes + 16; }
+
+__device__ inline int xcd_remap(int i, int n) {
+    const int x = i & 7, j = i >> 3, q = n >> 3, r = n & 7;
+    return x * q + min(x, r) + j;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The half-wave span [h*D/2, h*D/2 + D/2) of one global row into registers
+// (zeros when the row does not exist).
+template <typename T, int D>
+__device__ inline void load_span_global(const T *row, int h, bool valid, u32x4 *out) {
+    constexpr int NV = span_vecs<T, D>();
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(row) + h * (D / 2) * Ty<T>::kBytes);
+    if (valid) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) out[v] = p[v];
+    } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) out[v] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// The same span of row `row` of an LDS tile with pitch P.
+template <typename T, int D, int P>
+__device__ inline void load_span_lds(const char *tile, int row, int h, u32x4 *out) {
+    constexpr int NV = span_vecs<T, D>();
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(tile + row * P + h * (D / 2) * Ty<T>::kBytes);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) out[v] = p[v];
+}
+
+// Global -> registers -> LDS staging of kBN rows x D elements (rows >= nrows
+// are zero-filled).  Consecutive threads take consecutive 16-byte chunks of a
+// row, so a wave reads whole contiguous rows.
+template <typename T, int D, int P>
+struct Stager {
+    static constexpr int kVecPerRow = D * Ty<T>::kBytes / 16;
+    static constexpr int kVecs = kBN * kVecPerRow;
+    static_assert(kVecs % kThreads == 0, "tile must split evenly over the workgroup");
+    static constexpr int kPer = kVecs / kThreads;
+    u32x4 r[kPer];
+
+    __device__ inline void load(const T *base, int64_t stride_n, int row0, int nrows, int tid) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int c = tid + k * kThreads;
+            const int row = c / kVecPerRow, col = c % kVecPerRow;
+            const int gr = row0 + row;
+            if (gr < nrows) {
+                r[k] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base + (int64_t)gr * stride_n) + col * 16);
+            } else {
+                r[k] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    __device__ inline void store(char *tile, int tid) const {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int c = tid + k * kThreads;
+            const int row = c / kVecPerRow, col = c % kVecPerRow;
+            *reinterpret_cast<u32x4 *>(tile + row * P + col * 16) = r[k];
+        }
+    }
+};
+
+// Row index (within a 32-row tile) of accumulator element i of half-wave h.
+__device__ inline int acc_row(int i, int h) { return (i >> 2) * 8 + h * 4 + (i & 3); }
+
+// ================================================================= forward
+struct FwdParams {
+    const void *q_t, *k_t, *q_s, *k_s;
+    int64_t st[12];  // q_t(b,h,n), k_t(b,h,n), q_s(b,h,n), k_s(b,h,n), in elements
+    int H, n_q, n_k, n_qblk;
+    float tau_t, tau_s;
+    float *kl, *lse_t, *lse_s;
+};
+
+template <typename T, int DT, int DS, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void streamkl_fwd_kernel(FwdParams p) {
+    constexpr int PT = lds_pitch<T, DT>(), PS = lds_pitch<T, DS>();
+    constexpr int TILE_T = kBN * PT, TILE_S = kBN * PS, STAGE = TILE_T + TILE_S;
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int qb = p.n_qblk - 1 - (wg % p.n_qblk);
+    const int bh = wg / p.n_qblk, hh = bh % p.H, bb = bh / p.H;
+    const T *Qt = static_cast<const T *>(p.q_t) + bb * p.st[0] + hh * p.st[1];
+    const T *Kt = static_cast<const T *>(p.k_t) + bb * p.st[3] + hh * p.st[4];
+    const T *Qs = static_cast<const T *>(p.q_s) + bb * p.st[6] + hh * p.st[7];
+    const T *Ks = static_cast<const T *>(p.k_s) + bb * p.st[9] + hh * p.st[10];
+    const int64_t sqt = p.st[2], skt = p.st[5], sqs = p.st[8], sks = p.st[11];
+    const int n_q = p.n_q, n_k = p.n_k, off = n_k - n_q;
+
+    const int q0w = qb * kBlockX + w * kTile;  // first query of this wave
+    const int q = q0w + l32;                   // this lane's query
+    const bool qv = q < n_q;
+    const int qc = qv ? q : n_q - 1;
+    const bool wave_live = q0w < n_q;
+    const int qlast_w = min(n_q - 1, q0w + kTile - 1);
+
+    u32x4 qtv[span_vecs<T, DT>()], qsv[span_vecs<T, DS>()];
+    load_span_global<T, DT>(Qt + (int64_t)qc * sqt, hf, qv, qtv);
+    load_span_global<T, DS>(Qs + (int64_t)qc * sqs, hf, qv, qsv);
+
+    const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
+    // online state of this lane's query over the keys this half-wave sees
+    float mt = kMasked, lt = 0.f, at = 0.f, as = 0.f;  // teacher max, normaliser, sum e_t*x_t, sum e_t*x_s
+    float ms = kMasked, ls = 0.f;                      // student max, normaliser
+
+    const int qlast_wg = min(n_q - 1, qb * kBlockX + kBlockX - 1);
+    const int kend = CAUSAL ? min(n_k, qlast_wg + off + 1) : n_k;
+    const int ntile = (kend + kBN - 1) / kBN;
+
+    Stager<T, DT, PT> sgt;
+    Stager<T, DS, PS> sgs;
+    sgt.load(Kt, skt, 0, n_k, tid);
+    sgs.load(Ks, sks, 0, n_k, tid);
+    sgt.store(smem, tid);
+    sgs.store(smem + TILE_T, tid);
+    __syncthreads();
+
+    for (int it = 0; it < ntile; ++it) {
+        const char *bt = smem + (it & 1) * STAGE;
+        const char *bs = bt + TILE_T;
+        const bool more = it + 1 < ntile;
+        if (more) {
+            sgt.load(Kt, skt, (it + 1) * kBN, n_k, tid);
+            sgs.load(Ks, sks, (it + 1) * kBN, n_k, tid);
+        }
+        const int k0 = it * kBN;
+        const bool active = wave_live && (!CAUSAL || k0 <= qlast_w + off);
+        if (active) {
+            f32x16 acct = {}, accs = {};
+            {
+                u32x4 kv[span_vecs<T, DT>()];
+                load_span_lds<T, DT, PT>(bt, l32, hf, kv);
+#pragma unroll
+                for (int ks = 0; ks < Ty<T>::ksteps(DT); ++ks)
+                    acct = Ty<T>::mma(Ty<T>::frag(kv, ks), Ty<T>::frag(qtv, ks), acct);
+            }
+            {
+                u32x4 kv[span_vecs<T, DS>()];
+                load_span_lds<T, DS, PS>(bs, l32, hf, kv);
+#pragma unroll
+                for (int ks = 0; ks < Ty<T>::ksteps(DS); ++ks)
+                    accs = Ty<T>::mma(Ty<T>::frag(kv, ks), Ty<T>::frag(qsv, ks), accs);
+            }
+            const bool need_mask = (k0 + kBN > n_k) || (CAUSAL && k0 + kBN - 1 > q0w + off);
+            unsigned okbits = 0xffffu;
+            if (need_mask) {
+                okbits = 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + acc_row(i, hf);
+                    const bool ok = key < n_k && (!CAUSAL || key <= q + off);
+                    okbits |= ok ? (1u << i) : 0u;
+                    acct[i] = ok ? acct[i] : kMasked;
+                    accs[i] = ok ? accs[i] : kMasked;
+                }
+            }
+            float mxt = mt, mxs = ms;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mxt = fmaxf(mxt, acct[i]);
+                mxs = fmaxf(mxs, accs[i]);
+            }
+            const float rt = fast_exp2(ct * (mt - mxt));
+            const float rs = fast_exp2(cs * (ms - mxs));
+            lt *= rt; at *= rt; as *= rt; ls *= rs;
+            mt = mxt; ms = mxs;
+            const float nmt = -ct * mt, nms = -cs * ms;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float et = fast_exp2(fmaf(acct[i], ct, nmt));
+                float es = fast_exp2(fmaf(accs[i], cs, nms));
+                if (need_mask && !((okbits >> i) & 1u)) { et = 0.f; es = 0.f; }
+                lt += et;
+                ls += es;
+                at = fmaf(et, acct[i], at);
+                as = fmaf(et, accs[i], as);
+            }
+        }
+        if (more) {
+            char *nt = smem + ((it + 1) & 1) * STAGE;
+            sgt.store(nt, tid);
+            sgs.store(nt + TILE_T, tid);
+        }
+        __syncthreads();
+    }
+
+    // merge the two half-waves (same query, disjoint key subsets)
+    const float mt2 = __shfl_xor(mt, 32), lt2 = __shfl_xor(lt, 32);
+    const float at2 = __shfl_xor(at, 32), as2 = __shfl_xor(as, 32);
+    const float ms2 = __shfl_xor(ms, 32), ls2 = __shfl_xor(ls, 32);
+    const float m = fmaxf(mt, mt2);
+    const float w1 = fast_exp2(ct * (mt - m)), w2 = fast_exp2(ct * (mt2 - m));
+    const float L = lt * w1 + lt2 * w2;
+    const float AT = at * w1 + at2 * w2, AS = as * w1 + as2 * w2;
+    const float mS = fmaxf(ms, ms2);
+    const float v1 = fast_exp2(cs * (ms - mS)), v2 = fast_exp2(cs * (ms2 - mS));
+    const float LS = ls * v1 + ls2 * v2;
+    if (hf == 0 && qv) {
+        const float lse_t = p.tau_t * m + logf(L);
+        const float lse_s = p.tau_s * mS + logf(LS);
+        // E_{P_t}[s_t - s_s] - LSE_t + LSE_s
+        const float kl = (p.tau_t * AT - p.tau_s * AS) / L - lse_t + lse_s;
+        const int64_t row = ((int64_t)bb * p.H + hh) * n_q + q;
+        p.kl[row] = kl;
+        p.lse_t[row] = lse_t;
+        p.lse_s[row] = lse_s;
+    }
+}
+
+// Deterministic sum of n fp32 values (fixed order, fp64 accumulation), one block.
+__global__ __launch_bounds__(1024) void streamkl_sum_kernel(const float *x, int64_t n, float *out) {
+    __shared__ double red[1024];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) s += (double)x[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int k = 512; k > 0; k >>= 1) {
+        if ((int)threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = (float)red[0];
+}
+
+// ================================================================= backward
+// One kernel body serves both gradients.  DKMODE = false: the stationary items
+// x are queries and the streamed rows y are keys (output dq_s).  DKMODE = true:
+// x are keys and y are queries (output dk_s).
+struct BwdParams {
+    const void *x_t, *x_s, *y_t, *y_s;
+    int64_t st[12];  // x_t(b,h,n), x_s(b,h,n), y_t(b,h,n), y_s(b,h,n)
+    int H, n_x, n_y, n_q, n_k, n_xblk;
+    float tau_t, tau_s;
+    const float *lse_t, *lse_s, *g;
+    float g_scalar;
+    void *out;
+};
+
+template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE>
+__global__ __launch_bounds__(kThreads) void streamkl_bwd_kernel(BwdParams p) {
+    constexpr int PT = lds_pitch<T, DT>(), PS = lds_pitch<T, DS>();
+    constexpr int TILE_T = kBN * PT, TILE_S = kBN * PS;
+    constexpr int ROWV = DKMODE ? 3 * kBN * 4 : 0;  // per-query -LSE_t*log2e, -LSE_s*log2e, g*tau_s
+    constexpr int STAGE = TILE_T + TILE_S + ROWV;
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    // heaviest blocks first under a causal mask: high query blocks (dq) see the
+    // most keys, low key blocks (dk) are seen by the most queries
+    const int xb = DKMODE ? (wg % p.n_xblk) : (p.n_xblk - 1 - (wg % p.n_xblk));
+    const int bh = wg / p.n_xblk, hh = bh % p.H, bb = bh / p.H;
+    const T *Xt = static_cast<const T *>(p.x_t) + bb * p.st[0] + hh * p.st[1];
+    const T *Xs = static_cast<const T *>(p.x_s) + bb * p.st[3] + hh * p.st[4];
+    const T *Yt = static_cast<const T *>(p.y_t) + bb * p.st[6] + hh * p.st[7];
+    const T *Ys = static_cast<const T *>(p.y_s) + bb * p.st[9] + hh * p.st[10];
+    const int64_t sxt = p.st[2], sxs = p.st[5], syt = p.st[8], sys = p.st[11];
+    const int n_x = p.n_x, n_y = p.n_y, n_q = p.n_q, off = p.n_k - p.n_q;
+    const int64_t rowbase = ((int64_t)bb * p.H + hh) * n_q;  // per-query arrays of this head
+
+    const int x0w = xb * kBlockX + w * kTile;
+    const int x = x0w + l32;
+    const bool xv = x < n_x;
+    const int xc = xv ? x : n_x - 1;
+    const bool wave_live = x0w < n_x;
+
+    u32x4 xtv[span_vecs<T, DT>()], xsv[span_vecs<T, DS>()];
+    load_span_global<T, DT>(Xt + (int64_t)xc * sxt, hf, xv, xtv);
+    load_span_global<T, DS>(Xs + (int64_t)xc * sxs, hf, xv, xsv);
+
+    const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
+    float nlt = 0.f, nls = 0.f, gts = 0.f;  // per-lane row values (dq mode)
+    if (!DKMODE && xv) {
+        nlt = -p.lse_t[rowbase + x] * kLog2e;
+        nls = -p.lse_s[rowbase + x] * kLog2e;
+        gts = (p.g ? p.g[rowbase + x] : p.g_scalar) * p.tau_s;
+    }
+
+    f32x16 G[DS / kTile];
+#pragma unroll
+    for (int t = 0; t < DS / kTile; ++t) G[t] = f32x16{};
+
+    int ystart = 0, yend = n_y;
+    if (CAUSAL) {
+        if (!DKMODE) yend = min(p.n_k, min(n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
+        else ystart = (max(0, xb * kBlockX - off) / kBN) * kBN;
+    }
+    const int ntile = (yend - ystart + kBN - 1) / kBN;
+
+    Stager<T, DT, PT> sgt;
+    Stager<T, DS, PS> sgs;
+    float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query ystart + tid (tid < kBN)
+    auto load_rows = [&](int y0) {
+        if (DKMODE && tid < kBN) {
+            const int y = y0 + tid;
+            if (y < n_q) {
+                rv0 = -p.lse_t[rowbase + y] * kLog2e;
+                rv1 = -p.lse_s[rowbase + y] * kLog2e;
+                rv2 = (p.g ? p.g[rowbase + y] : p.g_scalar) * p.tau_s;
+            } else {
+                rv0 = 0.f; rv1 = 0.f; rv2 = 0.f;
+            }
+        }
+    };
+    auto store_rows = [&](char *stage) {
+        if (DKMODE && tid < kBN) {
+            float *rv = reinterpret_cast<float *>(stage + TILE_T + TILE_S);
+            rv[tid] = rv0;
+            rv[kBN + tid] = rv1;
+            rv[2 * kBN + tid] = rv2;
+        }
+    };
+
+    sgt.load(Yt, syt, ystart, n_y, tid);
+    sgs.load(Ys, sys, ystart, n_y, tid);
+    load_rows(ystart);
+    sgt.store(smem, tid);
+    sgs.store(smem + TILE_T, tid);
+    store_rows(smem);
+    __syncthreads();
+
+    for (int it = 0; it < ntile; ++it) {
+        const char *bt = smem + (it & 1) * STAGE;
+        const char *bs = bt + TILE_T;
+        const float *rv = reinterpret_cast<const float *>(bs + TILE_S);
+        const bool more = it + 1 < ntile;
+        const int y0 = ystart + it * kBN;
+        if (more) {
+            sgt.load(Yt, syt, y0 + kBN, n_y, tid);
+            sgs.load(Ys, sys, y0 + kBN, n_y, tid);
+            load_rows(y0 + kBN);
+        }
+        bool active = wave_live;
+        if (CAUSAL) {
+            if (!DKMODE) active = active && (y0 <= min(n_q - 1, x0w + kTile - 1) + off);
+            else active = active && (y0 + kBN - 1 + off >= x0w);
+        }
+        if (active) {
+            f32x16 acct = {}, accs = {};
+            {
+                u32x4 yv[span_vecs<T, DT>()];
+                load_span_lds<T, DT, PT>(bt, l32, hf, yv);
+#pragma unroll
+                for (int ks = 0; ks < Ty<T>::ksteps(DT); ++ks)
+                    acct = Ty<T>::mma(Ty<T>::frag(yv, ks), Ty<T>::frag(xtv, ks), acct);
+            }
+            {
+                u32x4 yv[span_vecs<T, DS>()];
+                load_span_lds<T, DS, PS>(bs, l32, hf, yv);
+#pragma unroll
+                for (int ks = 0; ks < Ty<T>::ksteps(DS); ++ks)
+                    accs = Ty<T>::mma(Ty<T>::frag(yv, ks), Ty<T>::frag(xsv, ks), accs);
+            }
+            bool need_mask = y0 + kBN > n_y;
+            if (CAUSAL) {
+                if (!DKMODE) need_mask = need_mask || (y0 + kBN - 1 > x0w + off);
+                else need_mask = need_mask || (x0w + kTile - 1 > y0 + off);
+            }
+            // dS[y][x] = g * tau_s * (P_s - P_t), kept in fp32
+            float dsv[16];
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                f32x4 a_t, a_s, gg;
+                if (DKMODE) {
+                    const int r0 = grp * 8 + hf * 4;
+                    a_t = *reinterpret_cast<const f32x4 *>(rv + r0);
+                    a_s = *reinterpret_cast<const f32x4 *>(rv + kBN + r0);
+                    gg = *reinterpret_cast<const f32x4 *>(rv + 2 * kBN + r0);
+                } else {
+                    a_t = f32x4{nlt, nlt, nlt, nlt};
+                    a_s = f32x4{nls, nls, nls, nls};
+                    gg = f32x4{gts, gts, gts, gts};
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = grp * 4 + e;
+                    const float pt = fast_exp2(fmaf(acct[i], ct, a_t[e]));
+                    const float ps = fast_exp2(fmaf(accs[i], cs, a_s[e]));
+                    float d = gg[e] * (ps - pt);
+                    if (need_mask) {
+                        const int y = y0 + acc_row(i, hf);
+                        bool ok = y < n_y;
+                        if (CAUSAL) ok = ok && (DKMODE ? (x <= y + off) : (y <= x + off));
+                        d = ok ? d : 0.f;
+                    }
+                    dsv[i] = d;
+                }
+            }
+            // G^T[d][x] += Y_s^T[d][y] . dS[y][x]
+            if constexpr (sizeof(T) == 2) {
+                const int trow = 4 * hf + ((lane & 15) >> 2);
+                const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    bf16x8 bfrag;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bfrag[e] = (bf16_t)dsv[ks * 8 + e];
+#pragma unroll
+                    for (int t = 0; t < DS / kTile; ++t) {
+                        const char *a0 = bs + (16 * ks + trow) * PS + (t * kTile + tcol) * 2;
+                        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4 *)(a0));
+                        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4 *)(a0 + 8 * PS));
+                        const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0), b1 = __builtin_bit_cast(bf16x4, v1);
+                        const bf16x8 afrag = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                        G[t] = Ty<bf16_t>::mma(afrag, bfrag, G[t]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < DS / kTile; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float a = *reinterpret_cast<const float *>(bs + acc_row(i, hf) * PS + (t * kTile + l32) * 4);
+                        G[t] = Ty<float>::mma(a, dsv[i], G[t]);
+                    }
+                }
+            }
+        }
+        if (more) {
+            char *nt = smem + ((it + 1) & 1) * STAGE;
+            sgt.store(nt, tid);
+            sgs.store(nt + TILE_T, tid);
+            store_rows(nt);
+        }
+        __syncthreads();
+    }
+
+    if (xv) {
+        T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.H + hh) * n_x + x) * DS;
+#pragma unroll
+        for (int t = 0; t < DS / kTile; ++t) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int d0 = t * kTile + grp * 8 + hf * 4;
+                if constexpr (sizeof(T) == 2) {
+                    bf16x4 o = {(bf16_t)G[t][grp * 4 + 0], (bf16_t)G[t][grp * 4 + 1], (bf16_t)G[t][grp * 4 + 2],
+                                (bf16_t)G[t][grp * 4 + 3]};
+                    *reinterpret_cast<bf16x4 *>(orow + d0) = o;
+                } else {
+                    f32x4 o = {G[t][grp * 4 + 0], G[t][grp * 4 + 1], G[t][grp * 4 + 2], G[t][grp * 4 + 3]};
+                    *reinterpret_cast<f32x4 *>(orow + d0) = o;
+                }
+            }
+        }
+    }
+}
+
+// ================================================================= host side
+struct Shape {
+    int B, H, n_q, n_k, d_t, d_s;
+};
+
+streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                             streamkl_dtype dtype, const Shape &s, const int64_t *strides, float tau_t,
+                             float tau_s, int causal, int64_t st[12]) {
+    if (!q_t || !k_t || !q_s || !k_s) return STREAMKL_ERR_INVALID;
+    if (dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) return STREAMKL_ERR_INVALID;
+    if (s.B < 1 || s.H < 1 || s.n_q < 1 || s.n_k < 1 || s.d_t < 1 || s.d_s < 1) return STREAMKL_ERR_INVALID;
+    if (!(tau_t >= 0.f) || !(tau_s >= 0.f) || !isfinite(tau_t) || !isfinite(tau_s)) return STREAMKL_ERR_INVALID;
+    if (causal != 0 && causal != 1) return STREAMKL_ERR_INVALID;
+    if (causal && s.n_q > s.n_k) return STREAMKL_ERR_INVALID;
+    if (!streamkl_supported(dtype, s.d_t, s.d_s)) return STREAMKL_ERR_UNSUPPORTED;
+    const int64_t elt = dtype == STREAMKL_BF16 ? 2 : 4;
+    // grid size and 32-bit row arithmetic inside the kernels
+    const int64_t nblk_q = ((int64_t)s.n_q + kBlockX - 1) / kBlockX, nblk_k = ((int64_t)s.n_k + kBlockX - 1) / kBlockX;
+    if ((int64_t)s.B * s.H * (nblk_q > nblk_k ? nblk_q : nblk_k) > (int64_t)INT32_MAX) return STREAMKL_ERR_INVALID;
+    if ((int64_t)s.n_q + kBlockX > (int64_t)INT32_MAX / 2 || (int64_t)s.n_k + kBlockX > (int64_t)INT32_MAX / 2)
+        return STREAMKL_ERR_INVALID;
+    const int dims[4] = {s.d_t, s.d_t, s.d_s, s.d_s};
+    const int ns[4] = {s.n_q, s.n_k, s.n_q, s.n_k};
+    const void *ptrs[4] = {q_t, k_t, q_s, k_s};
+    for (int t = 0; t < 4; ++t) {
+        if (strides) {
+            st[3 * t + 0] = strides[3 * t + 0];
+            st[3 * t + 1] = strides[3 * t + 1];
+            st[3 * t + 2] = strides[3 * t + 2];
+            if (st[3 * t + 0] < 0 || st[3 * t + 1] < 0 || st[3 * t + 2] < dims[t]) return STREAMKL_ERR_INVALID;
+        } else {
+            st[3 * t + 2] = dims[t];
+            st[3 * t + 1] = (int64_t)ns[t] * dims[t];
+            st[3 * t + 0] = (int64_t)s.H * ns[t] * dims[t];
+        }
+        if (((uintptr_t)ptrs[t]) % 16 != 0) return STREAMKL_ERR_INVALID;
+        for (int k = 0; k < 3; ++k)
+            if ((st[3 * t + k] * elt) % 16 != 0) return STREAMKL_ERR_INVALID;
+    }
+    return STREAMKL_OK;
+}
+
+typedef void (*fwd_launch_t)(const FwdParams &, int grid, hipStream_t);
+typedef void (*bwd_launch_t)(const BwdParams &, int grid, hipStream_t);
+
+template <typename T, int DT, int DS, bool C>
+void launch_fwd(const FwdParams &p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((streamkl_fwd_kernel<T, DT, DS, C>), dim3(grid), dim3(kThreads), 0, s, p);
+}
+template <typename T, int DT, int DS, bool C, bool DK>
+void launch_bwd(const BwdParams &p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C, DK>), dim3(grid), dim3(kThreads), 0, s, p);
+}
+
+template <typename T, int DT, int DS>
+fwd_launch_t pick_fwd2(int causal) {
+    return causal ? launch_fwd<T, DT, DS, true> : launch_fwd<T, DT, DS, false>;
+}
+template <typename T, int DT, int DS>
+bwd_launch_t pick_bwd2(int causal, bool dk) {
+    if (causal) return dk ? launch_bwd<T, DT, DS, true, true> : launch_bwd<T, DT, DS, true, false>;
+    return dk ? launch_bwd<T, DT, DS, false, true> : launch_bwd<T, DT, DS, false, false>;
+}
+template <typename T>
+fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
+    if (d_t == 64 && d_s == 64) return pick_fwd2<T, 64, 64>(causal);
+    if (d_t == 64 && d_s == 128) return pick_fwd2<T, 64, 128>(causal);
+    if (d_t == 128 && d_s == 64) return pick_fwd2<T, 128, 64>(causal);
+    if (d_t == 128 && d_s == 128) return pick_fwd2<T, 128, 128>(causal);
+    return nullptr;
+}
+template <typename T>
+bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool dk) {
+    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal, dk);
+    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal, dk);
+    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal, dk);
+    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal, dk);
+    return nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int streamkl_supported(streamkl_dtype dtype, int d_t, int d_s) {
+    if (dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) return 0;
+    const bool dt_ok = d_t == 64 || d_t == 128, ds_ok = d_s == 64 || d_s == 128;
+    return dt_ok && ds_ok ? 1 : 0;
+}
+
+const char *streamkl_status_string(streamkl_status status) {
+    switch (status) {
+        case STREAMKL_OK: return "ok";
+        case STREAMKL_ERR_INVALID: return "invalid argument";
+        case STREAMKL_ERR_UNSUPPORTED: return "unsupported head dimension / dtype combination";
+        case STREAMKL_ERR_WORKSPACE: return "workspace too small";
+        case STREAMKL_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+size_t streamkl_bwd_workspace_size(int B, int H, int n_q, int n_k, int d_t, int d_s, streamkl_dtype dtype,
+                                   int causal) {
+    (void)B; (void)H; (void)n_q; (void)n_k; (void)d_t; (void)d_s; (void)dtype; (void)causal;
+    return 0;
+}
+
+streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                             streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                             const int64_t *strides, float tau_t, float tau_s, int causal, float *kl_rows,
+                             float *lse_t, float *lse_s, float *kl_sum, void *stream) {
+    const Shape s{B, H, n_q, n_k, d_t, d_s};
+    FwdParams p{};
+    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, p.st);
+    if (rc != STREAMKL_OK) return rc;
+    if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
+    p.q_t = q_t; p.k_t = k_t; p.q_s = q_s; p.k_s = k_s;
+    p.H = H; p.n_q = n_q; p.n_k = n_k;
+    p.n_qblk = (n_q + kBlockX - 1) / kBlockX;
+    p.tau_t = tau_t; p.tau_s = tau_s;
+    p.kl = kl_rows; p.lse_t = lse_t; p.lse_s = lse_s;
+    fwd_launch_t fn = dtype == STREAMKL_BF16 ? pick_fwd1<bf16_t>(d_t, d_s, causal) : pick_fwd1<float>(d_t, d_s, causal);
+    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int grid = B * H * p.n_qblk;
+    fn(p, grid, hs);
+    if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    if (kl_sum) {
+        hipLaunchKernelGGL(streamkl_sum_kernel, dim3(1), dim3(1024), 0, hs, (const float *)kl_rows,
+                           (int64_t)B * H * n_q, kl_sum);
+        if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    }
+    return STREAMKL_OK;
+}
+
+streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                             streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                             const int64_t *strides, float tau_t, float tau_s, int causal, const float *lse_t,
+                             const float *lse_s, const float *grad_rows, float grad_scalar, void *dq_s,
+                             void *dk_s, void *stream) {
+    const Shape s{B, H, n_q, n_k, d_t, d_s};
+    int64_t st[12];
+    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, st);
+    if (rc != STREAMKL_OK) return rc;
+    if (!lse_t || !lse_s || !dq_s || !dk_s) return STREAMKL_ERR_INVALID;
+    if (!isfinite(grad_scalar)) return STREAMKL_ERR_INVALID;
+    if (((uintptr_t)dq_s) % 16 != 0 || ((uintptr_t)dk_s) % 16 != 0) return STREAMKL_ERR_INVALID;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool bf = dtype == STREAMKL_BF16;
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool dk = pass == 1;
+        BwdParams p{};
+        // stationary operand first, streamed second
+        const int xi = dk ? 1 : 0, yi = dk ? 0 : 1;  // 0 = queries, 1 = keys (index into q_t/k_t stride groups)
+        const void *tq[2] = {q_t, k_t}, *sq[2] = {q_s, k_s};
+        p.x_t = tq[xi]; p.x_s = sq[xi]; p.y_t = tq[yi]; p.y_s = sq[yi];
+        for (int k = 0; k < 3; ++k) {
+            p.st[0 + k] = st[3 * xi + k];        // teacher of the stationary kind
+            p.st[3 + k] = st[3 * (2 + xi) + k];  // student of the stationary kind
+            p.st[6 + k] = st[3 * yi + k];
+            p.st[9 + k] = st[3 * (2 + yi) + k];
+        }
+        p.H = H; p.n_q = n_q; p.n_k = n_k;
+        p.n_x = dk ? n_k : n_q;
+        p.n_y = dk ? n_q : n_k;
+        p.n_xblk = (p.n_x + kBlockX - 1) / kBlockX;
+        p.tau_t = tau_t; p.tau_s = tau_s;
+        p.lse_t = lse_t; p.lse_s = lse_s; p.g = grad_rows; p.g_scalar = grad_scalar;
+        p.out = dk ? dk_s : dq_s;
+        bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal, dk) : pick_bwd1<float>(d_t, d_s, causal, dk);
+        if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+        fn(p, B * H * p.n_xblk, hs);
+        if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    }
+    return STREAMKL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+"""Benchmark of the fused attention-KL hot path on one MI355X.
+
+A step is one full pass of the path over one batch of synthetic inputs that is
+already resident in HBM: the forward kernel (per-row online state, per-row KL
+and log-normalisers), the deterministic KL-sum reduction, and the backward
+(recompute of both probability tiles, dQ_s and dK_s).  The default workload is
+B=2, H=16, N_Q=N_K=16384, d_t=d_s=128, bf16, non-causal, with a correlated
+student (Q_s = Q_t + 0.3 N(0,1), K_s = K_t + 0.3 N(0,1)).
+
+Reported value: algorithmic fwd+bwd TFLOP/s over the timed steps, counting only
+the contractions over unmasked (query, key) pairs: forward 2 pairs (d_t + d_s),
+backward 2 pairs (d_t + 3 d_s) (the two score recomputes, dQ_s and dK_s).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--no-baseline-mem]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD published)
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(w):
+    pairs = w.pairs
+    return 2.0 * pairs * (w.d_t + w.d_s), 2.0 * pairs * (w.d_t + 3 * w.d_s)
+
+
+def materialized_baseline_peak(w, d, torch):
+    """Peak HBM of the materialize-then-reduce pattern (log_softmax of both
+    full score matrices, elementwise KL, sum, autograd backward) for one
+    (batch, head) slice, scaled to the whole batch.  Returns bytes or None."""
+    import math
+    try:
+        q_t, k_t = d["q_t"][:1, :1].float(), d["k_t"][:1, :1].float()
+        q_s = d["q_s"][:1, :1].float().clone().requires_grad_(True)
+        k_s = d["k_s"][:1, :1].float().clone().requires_grad_(True)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        st = (q_t @ k_t.transpose(-1, -2).contiguous()) * w.tau_t
+        ss = (q_s @ k_s.transpose(-1, -2).contiguous()) * w.tau_s
+        if w.causal:
+            mask = torch.ones(w.n_q, w.n_k, dtype=torch.bool, device=st.device).tril(w.n_k - w.n_q)
+            st = st.masked_fill(~mask, -math.inf)
+            ss = ss.masked_fill(~mask, -math.inf)
+        lpt = torch.log_softmax(st, -1)
+        lps = torch.log_softmax(ss, -1)
+        pt = lpt.exp()
+        klr = torch.where(pt > 0, pt * (lpt - lps), torch.zeros_like(pt)).sum(-1)
+        klr.sum().backward()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        del st, ss, lpt, lps, pt, klr, q_s, k_s
+        torch.cuda.empty_cache()
+        return int(peak) * w.B * w.H
+    except RuntimeError:  # out of memory
+        torch.cuda.empty_cache()
+        return None
+
+
+def cpu_baseline(w, x):
+    """The fp64 oracle, as it stands, on a bounded slice of the same workload:
+    one head, the first 192 query rows against all N_K keys (full forward and
+    backward of that slice)."""
+    import numpy as np
+
+    import oracle
+    rows = min(w.n_q, 192)
+    sl = {k: np.ascontiguousarray(v[:1, :1, :rows] if k.startswith("q") else v[:1, :1], dtype=np.float64)
+          for k, v in x.items()}
+    if w.causal:  # keep the slice's rows at their bottom-right causal position
+        sl = {k: (np.ascontiguousarray(x[k][:1, :1, w.n_q - rows:], dtype=np.float64) if k.startswith("q") else v)
+              for k, v in sl.items()}
+    sw = w.resized(B=1, H=1, n_q=rows)
+    f, b = flops(sw)
+    t0 = time.perf_counter()
+    oracle.fwd(sl["q_t"], sl["k_t"], sl["q_s"], sl["k_s"], w.tau_t, w.tau_s, w.causal)
+    oracle.bwd(sl["q_t"], sl["k_t"], sl["q_s"], sl["k_s"], w.tau_t, w.tau_s, w.causal)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": (f + b) / dt / 1e12, "unit": "TFLOP/s", "cores": int(os.environ.get("OMP_NUM_THREADS", cores)),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"fp64 oracle fwd+bwd, 1 head, {rows} query rows x {w.n_k} keys "
+                      f"({(f + b) / 1e9:.1f} GFLOP algorithmic)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="corr_16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baseline-mem", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this primitive is measured on one GPU only; multi-GPU runs are not supported "
+              "(the per-(batch, head) work shards with no exchange but is not built for several GPUs)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_kl_divergence_amd as skl
+    from attention_kl_divergence_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    x = inputs.make(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = {k: torch.from_numpy(v).to(tdt).cuda() for k, v in x.items()}
+    F, Bw = flops(w)
+    B, H = w.B, w.H
+
+    # outputs preallocated once (the library itself allocates nothing)
+    dev = d["q_t"].device
+    kl = torch.empty((B, H, w.n_q), dtype=torch.float32, device=dev)
+    lt, ls = torch.empty_like(kl), torch.empty_like(kl)
+    tot = torch.empty((1,), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, H, w.n_q, w.d_s), dtype=tdt, device=dev)
+    dk = torch.empty((B, H, w.n_k, w.d_s), dtype=tdt, device=dev)
+    lib = skl.load_library()
+    code = skl.STREAMKL_BF16 if w.dtype == "bf16" else skl.STREAMKL_F32
+    ptr = {k: v.data_ptr() for k, v in d.items()}
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def fwd():
+        rc = lib.streamkl_fwd(ptr["q_t"], ptr["k_t"], ptr["q_s"], ptr["k_s"], code, B, H, w.n_q, w.n_k, w.d_t, w.d_s,
+                              None, w.tau_t, w.tau_s, int(w.causal), kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
+                              tot.data_ptr(), sp)
+        if rc:
+            raise RuntimeError(skl.status_string(rc))
+
+    def bwd():
+        rc = lib.streamkl_bwd(ptr["q_t"], ptr["k_t"], ptr["q_s"], ptr["k_s"], code, B, H, w.n_q, w.n_k, w.d_t,
+                              w.d_s, None, w.tau_t, w.tau_s, int(w.causal), lt.data_ptr(), ls.data_ptr(), None,
+                              1.0, dq.data_ptr(), dk.data_ptr(), sp)
+        if rc:
+            raise RuntimeError(skl.status_string(rc))
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup done", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        fwd()
+        evs[s][1].record(stream)
+        bwd()
+        evs[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_f = np.array([e[0].elapsed_time(e[1]) for e in evs])  # ms
+    t_b = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_step = wall * 1e3 / args.steps
+    value = (F + Bw) * args.steps / wall / 1e12
+    fwd_tf = F / (np.mean(t_f) * 1e-3) / 1e12
+    bwd_tf = Bw / (np.mean(t_b) * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    elt = 2 if w.dtype == "bf16" else 4
+    in_bytes = elt * B * H * (w.n_q + w.n_k) * (w.d_t + w.d_s)
+    extra_bytes = 8 * B * H * w.n_q  # saved log-normalisers: the only state between the passes
+    print(f"[bench] fwd {np.mean(t_f):.3f} ms ({fwd_tf:.1f} TF/s), bwd {np.mean(t_b):.3f} ms ({bwd_tf:.1f} TF/s)",
+          file=sys.stderr, flush=True)
+
+    dominant = "fwd" if np.mean(t_f) >= np.mean(t_b) else "bwd"
+    res = {
+        "metric": "fused attn-KL fwd+bwd TFLOP/s & % bf16 MFMA peak at N=16K,d=128; extra HBM bytes",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "n_q": w.n_q, "n_k": w.n_k, "d_t": w.d_t, "d_s": w.d_s,
+                   "causal": w.causal, "inputs": f"seeded {w.recipe} N(0,1)", "parallelism": "single GPU"},
+        "pct_peak": round(100.0 * value / peak, 2),
+        "fwd_ms": round(float(np.mean(t_f)), 4), "bwd_ms": round(float(np.mean(t_b)), 4),
+        "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
+        "extra_hbm_bytes": extra_bytes,
+        "input_bytes": in_bytes,
+        "roofline": {"bound": "mfma", "kernel": f"streamkl_{dominant}",
+                     "achieved": round(fwd_tf if dominant == "fwd" else bwd_tf, 2), "peak": peak,
+                     "unit": "TFLOP/s",
+                     "frac": round((fwd_tf if dominant == "fwd" else bwd_tf) / peak, 4), "traffic": None},
+    }
+    if not args.no_baseline_mem:
+        bpk = materialized_baseline_peak(w, d, torch)
+        res["materialized_baseline_peak_bytes"] = bpk
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded slice", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * streamkl.h -- C ABI of the fused attention-KL primitive for MI355X (gfx950).
+ *
+ * What it computes.  For every query row r = (b, h, i) the forward KL divergence
+ * between the teacher and the student attention distributions over the keys,
+ * teacher first, in nats:
+ *
+ *     s_t[j] = tau_t * (Q_t[i] . K_t[j]),      s_s[j] = tau_s * (Q_s[i] . K_s[j])
+ *     P_t = softmax_j(s_t),                    P_s = softmax_j(s_s)
+ *     KL_r = sum_j P_t[j] * (log P_t[j] - log P_s[j])
+ *
+ * The quantity and its use as a distillation loss are those of "StreamKL: Fast
+ * and Memory-Efficient KL Divergence for Boosting Attention Distillation"
+ * (abstract: KL between two attention distributions, reduced without
+ * materialising either N_Q x N_K matrix; forward in one streaming pass, backward
+ * recomputing the probabilities tile by tile).  The direction (teacher in the
+ * first slot), the natural log and the temperature reading tau = 1/(sqrt(d) T)
+ * follow "Lecture 05 - Where It All Lands", section 3.1 (forward KL at
+ * temperature T); a T^2 or alpha weighting (section 3.3) is applied by the caller
+ * through the upstream gradient of streamkl_bwd.
+ *
+ * Causal masking, when requested, is bottom-right aligned: key j is allowed for
+ * query i iff j <= i + (n_k - n_q).  Causal with n_q > n_k is rejected (it would
+ * leave rows with no key).  Masked keys are excluded from both softmaxes.
+ *
+ * Conventions common to every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, frees nothing, never synchronises, and keeps no mutable
+ *    global state; it is safe to call from several host threads.
+ *  - Inputs are [B, H, N, d] with the last dimension contiguous.  `strides`
+ *    gives, in ELEMENTS, the batch, head and row strides of q_t, k_t, q_s, k_s in
+ *    that order (12 values: q_t.b, q_t.h, q_t.n, k_t.b, ...); NULL means fully
+ *    contiguous.  Every row must start on a 16-byte boundary.
+ *  - Teacher and student share dtype, B, H, n_q and n_k; d_t and d_s may differ.
+ *  - Per-row outputs (kl_rows, lse_t, lse_s, grad_rows) are contiguous fp32
+ *    [B, H, n_q].  Gradients dq_s / dk_s are contiguous [B, H, n_q | n_k, d_s]
+ *    in the input dtype and are overwritten, not accumulated.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it and the call returns before the work completes; a fault
+ *    during execution surfaces at the caller's next synchronisation.
+ *  - Every argument is validated on the host before any HIP call is made; an
+ *    error status means nothing was enqueued.
+ */
+#ifndef STREAMKL_H
+#define STREAMKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STREAMKL_OK = 0,
+    STREAMKL_ERR_INVALID = 1,     /* null pointer, bad size, bad tau, misalignment, causal with n_q > n_k */
+    STREAMKL_ERR_UNSUPPORTED = 2, /* (dtype, d_t, d_s) combination not built */
+    STREAMKL_ERR_WORKSPACE = 3,   /* reserved: workspace too small */
+    STREAMKL_ERR_HIP = 4          /* a HIP launch error was reported */
+} streamkl_status;
+
+typedef enum {
+    STREAMKL_F32 = 0,  /* fp32 inputs, fp32 MFMA (v_mfma_f32_32x32x2_f32) */
+    STREAMKL_BF16 = 1  /* bf16 inputs, bf16 MFMA with fp32 accumulation */
+} streamkl_dtype;
+
+/*
+ * Forward.  One streaming pass over the key tiles of every query block keeps,
+ * per query row, the teacher max m_t and normaliser l_t, the student max m_s and
+ * normaliser l_s, and the teacher-weighted score accumulators, and finishes with
+ *     KL = E_{P_t}[s_t - s_s] - LSE_t + LSE_s.
+ *
+ *   q_t, k_t  teacher queries [B,H,n_q,d_t] and keys [B,H,n_k,d_t]
+ *   q_s, k_s  student queries [B,H,n_q,d_s] and keys [B,H,n_k,d_s]
+ *   tau_t, tau_s  score scales (finite, >= 0; tau = 0 gives a uniform row)
+ *   causal    0 or 1
+ *   kl_rows   out, per-row KL (nats)
+ *   lse_t, lse_s  out, per-row log-normalisers log sum_j exp(s[j]); needed by
+ *             streamkl_bwd.  These 8 bytes per row are the only state kept
+ *             between the passes.
+ *   kl_sum    out, one fp32 device scalar = deterministic sum of kl_rows
+ *             (fixed reduction order, fp64 accumulation); may be NULL.
+ *
+ * Supported (d_t, d_s): each of 64 and 128, for both dtypes.
+ */
+streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                             streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                             const int64_t *strides, float tau_t, float tau_s, int causal,
+                             float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
+                             void *stream);
+
+/*
+ * Backward.  Gradients of L = sum_r g_r KL_r with respect to the student
+ * queries and keys; the teacher is a fixed target and gets no gradient.  The
+ * probabilities are recomputed tile by tile from the saved log-normalisers:
+ *     dS[i][j] = g_r * tau_s * (P_s[j] - P_t[j])      (0 for masked keys)
+ *     dq_s[i]  = sum_j dS[i][j] k_s[j],     dk_s[j] = sum_i dS[i][j] q_s[i]
+ *
+ *   q_t ... causal   exactly as passed to streamkl_fwd
+ *   lse_t, lse_s     the forward's outputs for the same inputs
+ *   grad_rows        [B,H,n_q] fp32 upstream gradient dL/dKL_r, or NULL to use
+ *                    grad_scalar for every row (1.0 for L = kl_sum)
+ *   dq_s, dk_s       out, input dtype, contiguous
+ *
+ * No workspace is used: dq_s and dk_s come from two deterministic kernels
+ * (query-major and key-major), with no atomics.
+ */
+streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                             streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                             const int64_t *strides, float tau_t, float tau_s, int causal,
+                             const float *lse_t, const float *lse_s,
+                             const float *grad_rows, float grad_scalar,
+                             void *dq_s, void *dk_s, void *stream);
+
+/* Bytes of device memory, beyond the caller's inputs and required outputs, that
+ * the library needs for a call of this shape: always 0 here (the saved
+ * log-normalisers are an output of streamkl_fwd). */
+size_t streamkl_bwd_workspace_size(int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                   streamkl_dtype dtype, int causal);
+
+/* Static, human-readable name of a status code. */
+const char *streamkl_status_string(streamkl_status status);
+
+/* 1 if (dtype, d_t, d_s) is built into this library, else 0. */
+int streamkl_supported(streamkl_dtype dtype, int d_t, int d_s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMKL_H */

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point include/streamkl.h declares, and rejects bad arguments with the
+documented status before making any HIP call (so fake device addresses are safe)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_kl_divergence_amd as skl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streamkl.h")
+
+A = 0x7f0000000000  # fake, 256-byte aligned "device" addresses; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(streamkl_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = skl.load_library()
+    names = declared_functions()
+    assert {"streamkl_fwd", "streamkl_bwd", "streamkl_bwd_workspace_size", "streamkl_status_string",
+            "streamkl_supported"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_support_matrix():
+    assert skl.status_string(0) == "ok"
+    assert "invalid" in skl.status_string(1)
+    assert "unsupported" in skl.status_string(2)
+    for code in (skl.STREAMKL_BF16, skl.STREAMKL_F32):
+        for dt in (64, 128):
+            for ds in (64, 128):
+                assert skl.supported(code, dt, ds)
+        assert not skl.supported(code, 96, 128)
+        assert not skl.supported(code, 128, 32)
+    assert not skl.supported(9, 128, 128)
+    assert skl.load_library().streamkl_bwd_workspace_size(2, 16, 16384, 16384, 128, 128, 1, 0) == 0
+
+
+def fwd(**kw):
+    a = dict(q_t=A, k_t=A + 0x100000, q_s=A + 0x200000, k_s=A + 0x300000, dtype=skl.STREAMKL_BF16,
+             B=2, H=3, n_q=100, n_k=77, d_t=128, d_s=64, strides=None, tau_t=0.088, tau_s=0.125, causal=0,
+             kl=A + 0x400000, lt=A + 0x500000, ls=A + 0x600000, tot=None, stream=None)
+    a.update(kw)
+    st = None
+    if a["strides"] is not None:
+        st = (ctypes.c_int64 * 12)(*a["strides"])
+    return skl.load_library().streamkl_fwd(a["q_t"], a["k_t"], a["q_s"], a["k_s"], a["dtype"], a["B"], a["H"],
+                                           a["n_q"], a["n_k"], a["d_t"], a["d_s"], st, a["tau_t"], a["tau_s"],
+                                           a["causal"], a["kl"], a["lt"], a["ls"], a["tot"], a["stream"])
+
+
+def bwd(**kw):
+    a = dict(q_t=A, k_t=A + 0x100000, q_s=A + 0x200000, k_s=A + 0x300000, dtype=skl.STREAMKL_BF16,
+             B=2, H=3, n_q=100, n_k=77, d_t=128, d_s=64, strides=None, tau_t=0.088, tau_s=0.125, causal=0,
+             lt=A + 0x500000, ls=A + 0x600000, g=None, gs=1.0, dq=A + 0x700000, dk=A + 0x800000, stream=None)
+    a.update(kw)
+    return skl.load_library().streamkl_bwd(a["q_t"], a["k_t"], a["q_s"], a["k_s"], a["dtype"], a["B"], a["H"],
+                                           a["n_q"], a["n_k"], a["d_t"], a["d_s"], None, a["tau_t"], a["tau_s"],
+                                           a["causal"], a["lt"], a["ls"], a["g"], a["gs"], a["dq"], a["dk"],
+                                           a["stream"])
+
+
+INV, UNS = skl.STREAMKL_ERR_INVALID, skl.STREAMKL_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_t=None), INV), (dict(k_s=None), INV), (dict(kl=None), INV), (dict(lt=None), INV),
+    (dict(B=0), INV), (dict(H=-1), INV), (dict(n_q=0), INV), (dict(n_k=0), INV),
+    (dict(tau_t=-0.1), INV), (dict(tau_s=float("nan")), INV), (dict(tau_t=float("inf")), INV),
+    (dict(causal=1), INV),            # n_q = 100 > n_k = 77
+    (dict(causal=2, n_k=200), INV),
+    (dict(dtype=5), INV),
+    (dict(d_t=96), UNS), (dict(d_s=32), UNS), (dict(d_t=0), INV),
+    (dict(q_s=A + 8), INV),           # not 16-byte aligned
+    (dict(strides=[3 * 100 * 128, 100 * 128, 120] + [0, 0, 128] * 3), INV),  # 120 bf16 = 240 B ok, k_t b/h 0 ok ...
+    (dict(strides=[3 * 100 * 128, 100 * 128, 100] + [0, 0, 128] * 3), INV),  # row stride < d_t
+    (dict(strides=[3 * 100 * 128, 100 * 128, 132] + [0, 0, 128] * 3), INV),  # 264 B rows, not 16-B aligned
+])
+def test_fwd_rejects_bad_arguments_before_any_hip_call(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_bwd_rejects_bad_arguments_before_any_hip_call():
+    assert bwd(lt=None) == INV
+    assert bwd(dq=None) == INV
+    assert bwd(dk=A + 4) == INV
+    assert bwd(gs=float("nan")) == INV
+    assert bwd(causal=1) == INV
+    assert bwd(d_s=80) == UNS
+    assert bwd(tau_s=-1.0) == INV
+
+
+def test_python_binding_fails_loudly_without_device_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        skl.streamkl_fwd(x, x, x, x)
