@@ -170,8 +170,80 @@ struct FwdParams {
     float *kl, *lse_t, *lse_s;
 };
 
+// Scheduler group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// C[y][x] = Y . X^T for one 32-row tile Y in LDS (pitch P) and this wave's
+// stationary fragments X.
+template <typename T, int D, int P>
+__device__ inline f32x16 tile_scores(const char *tile, const u32x4 *xv, int l32, int hf) {
+    u32x4 yv[span_vecs<T, D>()];
+    load_span_lds<T, D, P>(tile, l32, hf, yv);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < Ty<T>::ksteps(D); ++ks) acc = Ty<T>::mma(Ty<T>::frag(yv, ks), Ty<T>::frag(xv, ks), acc);
+    return acc;
+}
+
+// Online state of one query over the keys one half-wave sees.  Scores are kept
+// raw (x = q . k, unscaled); c = tau * log2(e) turns them into base-2 exponents.
+struct Online {
+    float mt, lt, at, as;  // teacher: running max of x_t, sum e_t, sum e_t x_t, sum e_t x_s
+    float ms, ls;          // student: running max of x_s, sum e_s
+};
+
+template <bool MASK, bool CAUSAL>
+__device__ inline void online_update(Online &o, f32x16 xt, f32x16 xs, float ct, float cs, int k0, int hf, int q,
+                                     int n_k, int off) {
+    unsigned okbits = 0xffffu;
+    if (MASK) {
+        okbits = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = k0 + acc_row(i, hf);
+            const bool ok = key < n_k && (!CAUSAL || key <= q + off);
+            okbits |= ok ? (1u << i) : 0u;
+            xt[i] = ok ? xt[i] : kMasked;
+            xs[i] = ok ? xs[i] : kMasked;
+        }
+    }
+    float mxt = o.mt, mxs = o.ms;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        mxt = fmaxf(mxt, xt[i]);
+        mxs = fmaxf(mxs, xs[i]);
+    }
+    const float rt = fast_exp2(ct * (o.mt - mxt));
+    const float rs = fast_exp2(cs * (o.ms - mxs));
+    o.mt = mxt;
+    o.ms = mxs;
+    const float nmt = -ct * mxt, nms = -cs * mxs;
+    float lt = 0.f, ls = 0.f, at = 0.f, as = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float et = fast_exp2(fmaf(xt[i], ct, nmt));
+        float es = fast_exp2(fmaf(xs[i], cs, nms));
+        if (MASK && !((okbits >> i) & 1u)) {
+            et = 0.f;
+            es = 0.f;
+        }
+        lt += et;
+        ls += es;
+        at = fmaf(et, xt[i], at);
+        as = fmaf(et, xs[i], as);
+    }
+    o.lt = fmaf(o.lt, rt, lt);
+    o.at = fmaf(o.at, rt, at);
+    o.as = fmaf(o.as, rt, as);
+    o.ls = fmaf(o.ls, rs, ls);
+}
+
+// One block = 4 waves x 32 queries.  The key tiles stream through a two-stage
+// LDS ring; in steady state the MFMAs of tile j+1 are issued interleaved with
+// the exponentials and sums of tile j (which only need registers), and the
+// global loads of tile j+3 are in flight meanwhile.
 template <typename T, int DT, int DS, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void streamkl_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd_kernel(FwdParams p) {
     constexpr int PT = lds_pitch<T, DT>(), PS = lds_pitch<T, DS>();
     constexpr int TILE_T = kBN * PT, TILE_S = kBN * PS, STAGE = TILE_T + TILE_S;
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
@@ -199,13 +271,13 @@ __global__ __launch_bounds__(kThreads) void streamkl_fwd_kernel(FwdParams p) {
     load_span_global<T, DS>(Qs + (int64_t)qc * sqs, hf, qv, qsv);
 
     const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
-    // online state of this lane's query over the keys this half-wave sees
-    float mt = kMasked, lt = 0.f, at = 0.f, as = 0.f;  // teacher max, normaliser, sum e_t*x_t, sum e_t*x_s
-    float ms = kMasked, ls = 0.f;                      // student max, normaliser
+    Online o{kMasked, 0.f, 0.f, 0.f, kMasked, 0.f};
 
     const int qlast_wg = min(n_q - 1, qb * kBlockX + kBlockX - 1);
     const int kend = CAUSAL ? min(n_k, qlast_wg + off + 1) : n_k;
     const int ntile = (kend + kBN - 1) / kBN;
+    auto active = [&](int t) { return wave_live && (!CAUSAL || t * kBN <= qlast_w + off); };
+    auto need_mask = [&](int t) { return (t * kBN + kBN > n_k) || (CAUSAL && t * kBN + kBN - 1 > q0w + off); };
 
     Stager<T, DT, PT> sgt;
     Stager<T, DS, PS> sgs;
@@ -213,88 +285,82 @@ __global__ __launch_bounds__(kThreads) void streamkl_fwd_kernel(FwdParams p) {
     sgs.load(Ks, sks, 0, n_k, tid);
     sgt.store(smem, tid);
     sgs.store(smem + TILE_T, tid);
+    if (ntile > 1) {
+        sgt.load(Kt, skt, kBN, n_k, tid);
+        sgs.load(Ks, sks, kBN, n_k, tid);
+        sgt.store(smem + STAGE, tid);
+        sgs.store(smem + STAGE + TILE_T, tid);
+    }
     __syncthreads();
+    if (ntile > 2) {
+        sgt.load(Kt, skt, 2 * kBN, n_k, tid);
+        sgs.load(Ks, sks, 2 * kBN, n_k, tid);
+    }
+    f32x16 xt0 = {}, xs0 = {}, xt1 = {}, xs1 = {};
+    if (active(0)) {
+        xt0 = tile_scores<T, DT, PT>(smem, qtv, l32, hf);
+        xs0 = tile_scores<T, DS, PS>(smem + TILE_T, qsv, l32, hf);
+    }
+    __syncthreads();  // every wave is done with stage 0 before tile 2 lands there
 
-    for (int it = 0; it < ntile; ++it) {
-        const char *bt = smem + (it & 1) * STAGE;
-        const char *bs = bt + TILE_T;
-        const bool more = it + 1 < ntile;
-        if (more) {
-            sgt.load(Kt, skt, (it + 1) * kBN, n_k, tid);
-            sgs.load(Ks, sks, (it + 1) * kBN, n_k, tid);
-        }
+    // softmax of tile `it` (registers cur_*) + scores of tile it+1 (into nxt_*)
+    auto step = [&](int it, f32x16 &cur_t, f32x16 &cur_s, f32x16 &nxt_t, f32x16 &nxt_s) {
+        const bool a_cur = active(it);
+        const bool a_nxt = it + 1 < ntile && active(it + 1);
+        const bool m_cur = need_mask(it);
+        const char *bn = smem + ((it + 1) & 1) * STAGE;
         const int k0 = it * kBN;
-        const bool active = wave_live && (!CAUSAL || k0 <= qlast_w + off);
-        if (active) {
-            f32x16 acct = {}, accs = {};
-            {
-                u32x4 kv[span_vecs<T, DT>()];
-                load_span_lds<T, DT, PT>(bt, l32, hf, kv);
+        if (a_cur && a_nxt && !m_cur) {
+            nxt_t = tile_scores<T, DT, PT>(bn, qtv, l32, hf);
+            nxt_s = tile_scores<T, DS, PS>(bn + TILE_T, qsv, l32, hf);
+            online_update<false, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
+            if constexpr (sizeof(T) == 2) {
+                constexpr int NM = Ty<T>::ksteps(DT) + Ty<T>::ksteps(DS);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NM, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, 12, 0);
 #pragma unroll
-                for (int ks = 0; ks < Ty<T>::ksteps(DT); ++ks)
-                    acct = Ty<T>::mma(Ty<T>::frag(kv, ks), Ty<T>::frag(qtv, ks), acct);
-            }
-            {
-                u32x4 kv[span_vecs<T, DS>()];
-                load_span_lds<T, DS, PS>(bs, l32, hf, kv);
-#pragma unroll
-                for (int ks = 0; ks < Ty<T>::ksteps(DS); ++ks)
-                    accs = Ty<T>::mma(Ty<T>::frag(kv, ks), Ty<T>::frag(qsv, ks), accs);
-            }
-            const bool need_mask = (k0 + kBN > n_k) || (CAUSAL && k0 + kBN - 1 > q0w + off);
-            unsigned okbits = 0xffffu;
-            if (need_mask) {
-                okbits = 0;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + acc_row(i, hf);
-                    const bool ok = key < n_k && (!CAUSAL || key <= q + off);
-                    okbits |= ok ? (1u << i) : 0u;
-                    acct[i] = ok ? acct[i] : kMasked;
-                    accs[i] = ok ? accs[i] : kMasked;
+                for (int k = 0; k < NM; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 9, 0);
                 }
             }
-            float mxt = mt, mxs = ms;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                mxt = fmaxf(mxt, acct[i]);
-                mxs = fmaxf(mxs, accs[i]);
+        } else {
+            if (a_nxt) {
+                nxt_t = tile_scores<T, DT, PT>(bn, qtv, l32, hf);
+                nxt_s = tile_scores<T, DS, PS>(bn + TILE_T, qsv, l32, hf);
             }
-            const float rt = fast_exp2(ct * (mt - mxt));
-            const float rs = fast_exp2(cs * (ms - mxs));
-            lt *= rt; at *= rt; as *= rt; ls *= rs;
-            mt = mxt; ms = mxs;
-            const float nmt = -ct * mt, nms = -cs * ms;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float et = fast_exp2(fmaf(acct[i], ct, nmt));
-                float es = fast_exp2(fmaf(accs[i], cs, nms));
-                if (need_mask && !((okbits >> i) & 1u)) { et = 0.f; es = 0.f; }
-                lt += et;
-                ls += es;
-                at = fmaf(et, acct[i], at);
-                as = fmaf(et, accs[i], as);
+            if (a_cur) {
+                if (m_cur) online_update<true, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
+                else online_update<false, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
             }
         }
-        if (more) {
-            char *nt = smem + ((it + 1) & 1) * STAGE;
-            sgt.store(nt, tid);
-            sgs.store(nt + TILE_T, tid);
+        if (it + 2 < ntile) {
+            char *bs = smem + (it & 1) * STAGE;
+            sgt.store(bs, tid);
+            sgs.store(bs + TILE_T, tid);
+            if (it + 3 < ntile) {
+                sgt.load(Kt, skt, (it + 3) * kBN, n_k, tid);
+                sgs.load(Ks, sks, (it + 3) * kBN, n_k, tid);
+            }
         }
         __syncthreads();
+    };
+    for (int it = 0; it < ntile; it += 2) {
+        step(it, xt0, xs0, xt1, xs1);
+        if (it + 1 < ntile) step(it + 1, xt1, xs1, xt0, xs0);
     }
 
     // merge the two half-waves (same query, disjoint key subsets)
-    const float mt2 = __shfl_xor(mt, 32), lt2 = __shfl_xor(lt, 32);
-    const float at2 = __shfl_xor(at, 32), as2 = __shfl_xor(as, 32);
-    const float ms2 = __shfl_xor(ms, 32), ls2 = __shfl_xor(ls, 32);
-    const float m = fmaxf(mt, mt2);
-    const float w1 = fast_exp2(ct * (mt - m)), w2 = fast_exp2(ct * (mt2 - m));
-    const float L = lt * w1 + lt2 * w2;
-    const float AT = at * w1 + at2 * w2, AS = as * w1 + as2 * w2;
-    const float mS = fmaxf(ms, ms2);
-    const float v1 = fast_exp2(cs * (ms - mS)), v2 = fast_exp2(cs * (ms2 - mS));
-    const float LS = ls * v1 + ls2 * v2;
+    const float mt2 = __shfl_xor(o.mt, 32), lt2 = __shfl_xor(o.lt, 32);
+    const float at2 = __shfl_xor(o.at, 32), as2 = __shfl_xor(o.as, 32);
+    const float ms2 = __shfl_xor(o.ms, 32), ls2 = __shfl_xor(o.ls, 32);
+    const float m = fmaxf(o.mt, mt2);
+    const float w1 = fast_exp2(ct * (o.mt - m)), w2 = fast_exp2(ct * (mt2 - m));
+    const float L = o.lt * w1 + lt2 * w2;
+    const float AT = o.at * w1 + at2 * w2, AS = o.as * w1 + as2 * w2;
+    const float mS = fmaxf(o.ms, ms2);
+    const float v1 = fast_exp2(cs * (o.ms - mS)), v2 = fast_exp2(cs * (ms2 - mS));
+    const float LS = o.ls * v1 + ls2 * v2;
     if (hf == 0 && qv) {
         const float lse_t = p.tau_t * m + logf(L);
         const float lse_s = p.tau_s * mS + logf(LS);
@@ -307,11 +373,22 @@ __global__ __launch_bounds__(kThreads) void streamkl_fwd_kernel(FwdParams p) {
     }
 }
 
-// Deterministic sum of n fp32 values (fixed order, fp64 accumulation), one block.
+// Deterministic sum of n fp32 values, one block: each thread accumulates a
+// fixed, strided subset in fp64 with several loads in flight, then a fixed
+// tree combines the partial sums.
 __global__ __launch_bounds__(1024) void streamkl_sum_kernel(const float *x, int64_t n, float *out) {
     __shared__ double red[1024];
+    constexpr int U = 8;
     double s = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += 1024) s += (double)x[i];
+    int64_t i = threadIdx.x;
+    for (; i + (U - 1) * 1024 < n; i += U * 1024) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = x[i + u * 1024];
+#pragma unroll
+        for (int u = 0; u < U; ++u) s += (double)v[u];
+    }
+    for (; i < n; i += 1024) s += (double)x[i];
     red[threadIdx.x] = s;
     __syncthreads();
     for (int k = 512; k > 0; k >>= 1) {
