@@ -87,11 +87,8 @@ template <> struct Ty<float> {
     static constexpr int ksteps(int D) { return D / 2; }
 };
 
-// 16-byte vectors in one half-wave span of a D-wide row
+// 16-byte chunks in one half-wave span of a D-wide row
 template <typename T, int D> constexpr int span_vecs() { return D * Ty<T>::kBytes / 32; }
-// LDS row pitch: 16 bytes of padding keep the 32 rows of a 16-byte column read
-// on distinct banks
-template <typename T, int D> constexpr int lds_pitch() { return D * Ty<T>::kBytes + 16; }
 
 __device__ inline int xcd_remap(int i, int n) {
     const int x = i & 7, j = i >> 3, q = n >> 3, r = n & 7;
@@ -99,6 +96,50 @@ __device__ inline int xcd_remap(int i, int n) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile holds kBN rows of D elements back to back, without padding.  Each row
+// is a run of 16-byte chunks and chunk c of row r sits at position c ^ swz(r).
+// The swizzle keeps the two read patterns used on a tile free of bank conflicts
+// on the 64-bank LDS: 16 lanes reading the same chunk of 16 consecutive rows
+// (MFMA operand rows), and 16 lanes reading 32 contiguous bytes from each of 4
+// consecutive rows (the transpose reads of the backward).  Tiles are filled by
+// direct global->LDS loads, which place lane i's 16 bytes at slot base + 16 i,
+// so each lane fetches the global chunk that belongs at its slot.
+template <typename T, int D>
+struct Tile {
+    static constexpr int kRowBytes = D * Ty<T>::kBytes;
+    static constexpr int kChunks = kRowBytes / 16;  // 8, 16 or 32
+    static constexpr int kBytes = kBN * kRowBytes;
+    static_assert(kChunks == 8 || kChunks == 16 || kChunks == 32, "unsupported row width");
+    __device__ static inline int swz(int r) {
+        if constexpr (kChunks == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+        else return ((r & 3) << 2) | ((r >> 2) & 3);
+    }
+    __device__ static inline int chunk_off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
+};
+
+// Rows [row0, row0 + kBN) of a [n, D] row-major matrix (row stride in elements)
+// into an LDS tile, by direct global->LDS loads.  Rows past the end repeat the
+// last row: they are always masked out before use, and finite values keep
+// 0 * value = 0 in the contractions.
+template <typename T, int D>
+__device__ inline void dma_tile(const T *base, int64_t stride_n, int row0, int nrows, char *tile, int wv, int lane) {
+    using L = Tile<T, D>;
+    static_assert(L::kBytes % (1024 * kWaves) == 0, "tile must split evenly over the waves");
+    constexpr int kPerWave = L::kBytes / 1024 / kWaves;
+#pragma unroll
+    for (int k = 0; k < kPerWave; ++k) {
+        const int slot = wv * kPerWave + k;  // wave-uniform
+        const int pos = slot * 64 + lane;    // chunk slot this lane fills
+        const int r = pos / L::kChunks;
+        const int c = (pos % L::kChunks) ^ L::swz(r);
+        int gr = row0 + r;
+        gr = gr < nrows ? gr : nrows - 1;
+        const char *g = reinterpret_cast<const char *>(base + (int64_t)gr * stride_n) + c * 16;
+        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(tile + slot * 1024), 16, 0, 0);
+    }
+}
 
 // The half-wave span [h*D/2, h*D/2 + D/2) of one global row into registers
 // (zeros when the row does not exist).
@@ -115,48 +156,14 @@ __device__ inline void load_span_global(const T *row, int h, bool valid, u32x4 *
     }
 }
 
-// The same span of row `row` of an LDS tile with pitch P.
-template <typename T, int D, int P>
+// The same span of row `row` of an LDS tile.
+template <typename T, int D>
 __device__ inline void load_span_lds(const char *tile, int row, int h, u32x4 *out) {
     constexpr int NV = span_vecs<T, D>();
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(tile + row * P + h * (D / 2) * Ty<T>::kBytes);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) out[v] = p[v];
+    for (int v = 0; v < NV; ++v)
+        out[v] = *reinterpret_cast<const u32x4 *>(tile + Tile<T, D>::chunk_off(row, h * NV + v));
 }
-
-// Global -> registers -> LDS staging of kBN rows x D elements (rows >= nrows
-// are zero-filled).  Consecutive threads take consecutive 16-byte chunks of a
-// row, so a wave reads whole contiguous rows.
-template <typename T, int D, int P>
-struct Stager {
-    static constexpr int kVecPerRow = D * Ty<T>::kBytes / 16;
-    static constexpr int kVecs = kBN * kVecPerRow;
-    static_assert(kVecs % kThreads == 0, "tile must split evenly over the workgroup");
-    static constexpr int kPer = kVecs / kThreads;
-    u32x4 r[kPer];
-
-    __device__ inline void load(const T *base, int64_t stride_n, int row0, int nrows, int tid) {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int c = tid + k * kThreads;
-            const int row = c / kVecPerRow, col = c % kVecPerRow;
-            const int gr = row0 + row;
-            if (gr < nrows) {
-                r[k] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base + (int64_t)gr * stride_n) + col * 16);
-            } else {
-                r[k] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    }
-    __device__ inline void store(char *tile, int tid) const {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int c = tid + k * kThreads;
-            const int row = c / kVecPerRow, col = c % kVecPerRow;
-            *reinterpret_cast<u32x4 *>(tile + row * P + col * 16) = r[k];
-        }
-    }
-};
 
 // Row index (within a 32-row tile) of accumulator element i of half-wave h.
 __device__ inline int acc_row(int i, int h) { return (i >> 2) * 8 + h * 4 + (i & 3); }
@@ -175,10 +182,10 @@ constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 // C[y][x] = Y . X^T for one 32-row tile Y in LDS (pitch P) and this wave's
 // stationary fragments X.
-template <typename T, int D, int P>
+template <typename T, int D>
 __device__ inline f32x16 tile_scores(const char *tile, const u32x4 *xv, int l32, int hf) {
     u32x4 yv[span_vecs<T, D>()];
-    load_span_lds<T, D, P>(tile, l32, hf, yv);
+    load_span_lds<T, D>(tile, l32, hf, yv);
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < Ty<T>::ksteps(D); ++ks) acc = Ty<T>::mma(Ty<T>::frag(yv, ks), Ty<T>::frag(xv, ks), acc);
@@ -239,16 +246,18 @@ __device__ inline void online_update(Online &o, f32x16 xt, f32x16 xs, float ct, 
 }
 
 // One block = 4 waves x 32 queries.  The key tiles stream through a two-stage
-// LDS ring; in steady state the MFMAs of tile j+1 are issued interleaved with
-// the exponentials and sums of tile j (which only need registers), and the
-// global loads of tile j+3 are in flight meanwhile.
+// LDS ring filled by direct global->LDS loads; in steady state the MFMAs of
+// tile j+1 are issued interleaved with the exponentials and sums of tile j
+// (which only need registers) while the loads of tile j+2 are in flight.
 template <typename T, int DT, int DS, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd_kernel(FwdParams p) {
-    constexpr int PT = lds_pitch<T, DT>(), PS = lds_pitch<T, DS>();
-    constexpr int TILE_T = kBN * PT, TILE_S = kBN * PS, STAGE = TILE_T + TILE_S;
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    using TileT = Tile<T, DT>;
+    using TileS = Tile<T, DS>;
+    constexpr int STAGE = TileT::kBytes + TileS::kBytes;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int qb = p.n_qblk - 1 - (wg % p.n_qblk);
     const int bh = wg / p.n_qblk, hh = bh % p.H, bb = bh / p.H;
@@ -266,6 +275,19 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
     const bool wave_live = q0w < n_q;
     const int qlast_w = min(n_q - 1, q0w + kTile - 1);
 
+    const int qlast_wg = min(n_q - 1, qb * kBlockX + kBlockX - 1);
+    const int kend = CAUSAL ? min(n_k, qlast_wg + off + 1) : n_k;
+    const int ntile = (kend + kBN - 1) / kBN;
+    auto active = [&](int t) { return wave_live && (!CAUSAL || t * kBN <= qlast_w + off); };
+    auto need_mask = [&](int t) { return (t * kBN + kBN > n_k) || (CAUSAL && t * kBN + kBN - 1 > q0w + off); };
+    auto issue = [&](int t, char *stage) {
+        dma_tile<T, DT>(Kt, skt, t * kBN, n_k, stage, w, lane);
+        dma_tile<T, DS>(Ks, sks, t * kBN, n_k, stage + TileT::kBytes, w, lane);
+    };
+
+    issue(0, smem);
+    if (ntile > 1) issue(1, smem + STAGE);
+
     u32x4 qtv[span_vecs<T, DT>()], qsv[span_vecs<T, DS>()];
     load_span_global<T, DT>(Qt + (int64_t)qc * sqt, hf, qv, qtv);
     load_span_global<T, DS>(Qs + (int64_t)qc * sqs, hf, qv, qsv);
@@ -273,46 +295,25 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
     const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
     Online o{kMasked, 0.f, 0.f, 0.f, kMasked, 0.f};
 
-    const int qlast_wg = min(n_q - 1, qb * kBlockX + kBlockX - 1);
-    const int kend = CAUSAL ? min(n_k, qlast_wg + off + 1) : n_k;
-    const int ntile = (kend + kBN - 1) / kBN;
-    auto active = [&](int t) { return wave_live && (!CAUSAL || t * kBN <= qlast_w + off); };
-    auto need_mask = [&](int t) { return (t * kBN + kBN > n_k) || (CAUSAL && t * kBN + kBN - 1 > q0w + off); };
-
-    Stager<T, DT, PT> sgt;
-    Stager<T, DS, PS> sgs;
-    sgt.load(Kt, skt, 0, n_k, tid);
-    sgs.load(Ks, sks, 0, n_k, tid);
-    sgt.store(smem, tid);
-    sgs.store(smem + TILE_T, tid);
-    if (ntile > 1) {
-        sgt.load(Kt, skt, kBN, n_k, tid);
-        sgs.load(Ks, sks, kBN, n_k, tid);
-        sgt.store(smem + STAGE, tid);
-        sgs.store(smem + STAGE + TILE_T, tid);
-    }
     __syncthreads();
-    if (ntile > 2) {
-        sgt.load(Kt, skt, 2 * kBN, n_k, tid);
-        sgs.load(Ks, sks, 2 * kBN, n_k, tid);
-    }
     f32x16 xt0 = {}, xs0 = {}, xt1 = {}, xs1 = {};
     if (active(0)) {
-        xt0 = tile_scores<T, DT, PT>(smem, qtv, l32, hf);
-        xs0 = tile_scores<T, DS, PS>(smem + TILE_T, qsv, l32, hf);
+        xt0 = tile_scores<T, DT>(smem, qtv, l32, hf);
+        xs0 = tile_scores<T, DS>(smem + TileT::kBytes, qsv, l32, hf);
     }
     __syncthreads();  // every wave is done with stage 0 before tile 2 lands there
 
     // softmax of tile `it` (registers cur_*) + scores of tile it+1 (into nxt_*)
     auto step = [&](int it, f32x16 &cur_t, f32x16 &cur_s, f32x16 &nxt_t, f32x16 &nxt_s) {
+        if (it + 2 < ntile) issue(it + 2, smem + (it & 1) * STAGE);
         const bool a_cur = active(it);
         const bool a_nxt = it + 1 < ntile && active(it + 1);
         const bool m_cur = need_mask(it);
         const char *bn = smem + ((it + 1) & 1) * STAGE;
         const int k0 = it * kBN;
         if (a_cur && a_nxt && !m_cur) {
-            nxt_t = tile_scores<T, DT, PT>(bn, qtv, l32, hf);
-            nxt_s = tile_scores<T, DS, PS>(bn + TILE_T, qsv, l32, hf);
+            nxt_t = tile_scores<T, DT>(bn, qtv, l32, hf);
+            nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, qsv, l32, hf);
             online_update<false, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
             if constexpr (sizeof(T) == 2) {
                 constexpr int NM = Ty<T>::ksteps(DT) + Ty<T>::ksteps(DS);
@@ -326,21 +327,12 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
             }
         } else {
             if (a_nxt) {
-                nxt_t = tile_scores<T, DT, PT>(bn, qtv, l32, hf);
-                nxt_s = tile_scores<T, DS, PS>(bn + TILE_T, qsv, l32, hf);
+                nxt_t = tile_scores<T, DT>(bn, qtv, l32, hf);
+                nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, qsv, l32, hf);
             }
             if (a_cur) {
                 if (m_cur) online_update<true, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
                 else online_update<false, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
-            }
-        }
-        if (it + 2 < ntile) {
-            char *bs = smem + (it & 1) * STAGE;
-            sgt.store(bs, tid);
-            sgs.store(bs + TILE_T, tid);
-            if (it + 3 < ntile) {
-                sgt.load(Kt, skt, (it + 3) * kBN, n_k, tid);
-                sgs.load(Ks, sks, (it + 3) * kBN, n_k, tid);
             }
         }
         __syncthreads();
@@ -412,15 +404,104 @@ struct BwdParams {
     void *out;
 };
 
-template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE>
-__global__ __launch_bounds__(kThreads) void streamkl_bwd_kernel(BwdParams p) {
-    constexpr int PT = lds_pitch<T, DT>(), PS = lds_pitch<T, DS>();
-    constexpr int TILE_T = kBN * PT, TILE_S = kBN * PS;
-    constexpr int ROWV = DKMODE ? 3 * kBN * 4 : 0;  // per-query -LSE_t*log2e, -LSE_s*log2e, g*tau_s
-    constexpr int STAGE = TILE_T + TILE_S + ROWV;
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+// dS[y][x] = g * tau_s * (P_s - P_t) for one 32x32 tile, in fp32, with
+// P = 2^(x * c - LSE * log2 e).  Per-query values (-LSE_t log2 e, -LSE_s log2 e,
+// g tau_s) are per lane when the queries are the stationary items, else they
+// come from the stage's LDS row-value block rv[3][kBN].
+template <bool MASK, bool CAUSAL, bool DKMODE>
+__device__ inline void tile_ds(const f32x16 &xt, const f32x16 &xs, float ct, float cs, float nlt, float nls,
+                               float gts, const float *rv, int y0, int hf, int x, int n_y, int off, float *dsv) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+        f32x4 a_t, a_s, gg;
+        if (DKMODE) {
+            const int r0 = grp * 8 + hf * 4;
+            a_t = *reinterpret_cast<const f32x4 *>(rv + r0);
+            a_s = *reinterpret_cast<const f32x4 *>(rv + kBN + r0);
+            gg = *reinterpret_cast<const f32x4 *>(rv + 2 * kBN + r0);
+        } else {
+            a_t = f32x4{nlt, nlt, nlt, nlt};
+            a_s = f32x4{nls, nls, nls, nls};
+            gg = f32x4{gts, gts, gts, gts};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = grp * 4 + e;
+            const float pt = fast_exp2(fmaf(xt[i], ct, a_t[e]));
+            const float ps = fast_exp2(fmaf(xs[i], cs, a_s[e]));
+            float d = gg[e] * (ps - pt);
+            if (MASK) {
+                const int y = y0 + acc_row(i, hf);
+                bool ok = y < n_y;
+                if (CAUSAL) ok = ok && (DKMODE ? (x <= y + off) : (y <= x + off));
+                d = ok ? d : 0.f;
+            }
+            dsv[i] = d;
+        }
+    }
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+// G^T[d][x] += Y_s^T[d][y] . dS[y][x].  dS is the B operand straight from the
+// accumulator layout (its row order is the contraction order); the matching
+// transposed student rows come from the row-major LDS tile via
+// ds_read_b64_tr_b16 (fp32 inputs: one ds_read_b32 per k-step).
+template <typename T, int DS>
+__device__ inline void tile_grad(f32x16 *G, const float *dsv, const char *ys, int lane, int hf, int l32) {
+    using L = Tile<T, DS>;
+    if constexpr (sizeof(T) == 2) {
+        const int trow = 4 * hf + ((lane & 15) >> 2);
+        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 bfrag;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bfrag[e] = (bf16_t)dsv[ks * 8 + e];
+#pragma unroll
+            for (int t = 0; t < DS / kTile; ++t) {
+                const int r0 = 16 * ks + trow, col = t * kTile + tcol;
+                const char *a0 = ys + L::chunk_off(r0, col >> 3) + (col & 7) * 2;
+                const char *a1 = ys + L::chunk_off(r0 + 8, col >> 3) + (col & 7) * 2;
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(a0));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(a1));
+                const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0), b1 = __builtin_bit_cast(bf16x4, v1);
+                const bf16x8 afrag = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                G[t] = Ty<bf16_t>::mma(afrag, bfrag, G[t]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < DS / kTile; ++t) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = acc_row(i, hf), col = t * kTile + l32;
+                const float a = *reinterpret_cast<const float *>(ys + L::chunk_off(r, col >> 2) + (col & 3) * 4);
+                G[t] = Ty<float>::mma(a, dsv[i], G[t]);
+            }
+        }
+    }
+}
+
+#ifndef STREAMKL_BWD_PIPE
+#define STREAMKL_BWD_PIPE 0
+#endif
+// PIPE: three-stage LDS ring, the scores of tile j+1 are issued interleaved
+// with dS of tile j (one wave per SIMD, ILP inside the wave).  Otherwise a
+// two-stage ring with tile-at-a-time work and two waves per SIMD overlapping
+// each other's MFMA and VALU phases.
+constexpr bool kBwdPipe = STREAMKL_BWD_PIPE != 0;
+
+template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE>
+__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && !kBwdPipe) ? 2 : 1) void streamkl_bwd_kernel(BwdParams p) {
+    using TileT = Tile<T, DT>;
+    using TileS = Tile<T, DS>;
+    constexpr int NSTAGE = kBwdPipe ? 3 : 2;
+    constexpr int STAGE = TileT::kBytes + TileS::kBytes;
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    // dk mode: per-query -LSE_t log2 e, -LSE_s log2 e, g tau_s of each stage's rows
+    __shared__ __attribute__((aligned(16))) float rowv[DKMODE ? NSTAGE : 1][3][kBN];
+
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     // heaviest blocks first under a causal mask: high query blocks (dq) see the
     // most keys, low key blocks (dk) are seen by the most queries
@@ -440,6 +521,53 @@ __global__ __launch_bounds__(kThreads) void streamkl_bwd_kernel(BwdParams p) {
     const int xc = xv ? x : n_x - 1;
     const bool wave_live = x0w < n_x;
 
+    int ystart = 0, yend = n_y;
+    if (CAUSAL) {
+        if (!DKMODE) yend = min(p.n_k, min(n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
+        else ystart = (max(0, xb * kBlockX - off) / kBN) * kBN;
+    }
+    const int ntile = (yend - ystart + kBN - 1) / kBN;
+    auto active = [&](int t) {
+        const int y0 = ystart + t * kBN;
+        if (!wave_live) return false;
+        if (!CAUSAL) return true;
+        return DKMODE ? (y0 + kBN - 1 + off >= x0w) : (y0 <= min(n_q - 1, x0w + kTile - 1) + off);
+    };
+    auto need_mask = [&](int t) {
+        const int y0 = ystart + t * kBN;
+        bool m = y0 + kBN > n_y;
+        if (CAUSAL) m = m || (DKMODE ? (x0w + kTile - 1 > y0 + off) : (y0 + kBN - 1 > x0w + off));
+        return m;
+    };
+    auto issue = [&](int t, int stage) {
+        char *base = smem + stage * STAGE;
+        dma_tile<T, DT>(Yt, syt, ystart + t * kBN, n_y, base, w, lane);
+        dma_tile<T, DS>(Ys, sys, ystart + t * kBN, n_y, base + TileT::kBytes, w, lane);
+    };
+    float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query y0 + tid (tid < kBN)
+    auto load_rows = [&](int t) {
+        if (DKMODE && tid < kBN) {
+            const int y = ystart + t * kBN + tid;
+            rv0 = rv1 = rv2 = 0.f;
+            if (y < n_q) {
+                rv0 = -p.lse_t[rowbase + y] * kLog2e;
+                rv1 = -p.lse_s[rowbase + y] * kLog2e;
+                rv2 = (p.g ? p.g[rowbase + y] : p.g_scalar) * p.tau_s;
+            }
+        }
+    };
+    auto store_rows = [&](int stage) {
+        if (DKMODE && tid < kBN) {
+            rowv[stage][0][tid] = rv0;
+            rowv[stage][1][tid] = rv1;
+            rowv[stage][2][tid] = rv2;
+        }
+    };
+
+    issue(0, 0);
+    load_rows(0);
+    if (kBwdPipe && ntile > 1) issue(1, 1);
+
     u32x4 xtv[span_vecs<T, DT>()], xsv[span_vecs<T, DS>()];
     load_span_global<T, DT>(Xt + (int64_t)xc * sxt, hf, xv, xtv);
     load_span_global<T, DS>(Xs + (int64_t)xc * sxs, hf, xv, xsv);
@@ -456,151 +584,88 @@ __global__ __launch_bounds__(kThreads) void streamkl_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < DS / kTile; ++t) G[t] = f32x16{};
 
-    int ystart = 0, yend = n_y;
-    if (CAUSAL) {
-        if (!DKMODE) yend = min(p.n_k, min(n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
-        else ystart = (max(0, xb * kBlockX - off) / kBN) * kBN;
+    store_rows(0);
+    if (kBwdPipe && ntile > 1) {
+        load_rows(1);
+        store_rows(1);
     }
-    const int ntile = (yend - ystart + kBN - 1) / kBN;
-
-    Stager<T, DT, PT> sgt;
-    Stager<T, DS, PS> sgs;
-    float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query ystart + tid (tid < kBN)
-    auto load_rows = [&](int y0) {
-        if (DKMODE && tid < kBN) {
-            const int y = y0 + tid;
-            if (y < n_q) {
-                rv0 = -p.lse_t[rowbase + y] * kLog2e;
-                rv1 = -p.lse_s[rowbase + y] * kLog2e;
-                rv2 = (p.g ? p.g[rowbase + y] : p.g_scalar) * p.tau_s;
-            } else {
-                rv0 = 0.f; rv1 = 0.f; rv2 = 0.f;
-            }
-        }
-    };
-    auto store_rows = [&](char *stage) {
-        if (DKMODE && tid < kBN) {
-            float *rv = reinterpret_cast<float *>(stage + TILE_T + TILE_S);
-            rv[tid] = rv0;
-            rv[kBN + tid] = rv1;
-            rv[2 * kBN + tid] = rv2;
-        }
-    };
-
-    sgt.load(Yt, syt, ystart, n_y, tid);
-    sgs.load(Ys, sys, ystart, n_y, tid);
-    load_rows(ystart);
-    sgt.store(smem, tid);
-    sgs.store(smem + TILE_T, tid);
-    store_rows(smem);
     __syncthreads();
 
-    for (int it = 0; it < ntile; ++it) {
-        const char *bt = smem + (it & 1) * STAGE;
-        const char *bs = bt + TILE_T;
-        const float *rv = reinterpret_cast<const float *>(bs + TILE_S);
-        const bool more = it + 1 < ntile;
+    auto ds_grad = [&](const f32x16 &cur_t, const f32x16 &cur_s, int it, int stage, bool m_cur) {
         const int y0 = ystart + it * kBN;
-        if (more) {
-            sgt.load(Yt, syt, y0 + kBN, n_y, tid);
-            sgs.load(Ys, sys, y0 + kBN, n_y, tid);
-            load_rows(y0 + kBN);
+        const float *rv = &rowv[DKMODE ? stage : 0][0][0];
+        float dsv[16];
+        if (m_cur) tile_ds<true, CAUSAL, DKMODE>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
+        else tile_ds<false, CAUSAL, DKMODE>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
+        tile_grad<T, DS>(G, dsv, smem + stage * STAGE + TileT::kBytes, lane, hf, l32);
+    };
+
+    if constexpr (kBwdPipe) {
+        f32x16 xt0 = {}, xs0 = {}, xt1 = {}, xs1 = {};
+        if (active(0)) {
+            xt0 = tile_scores<T, DT>(smem, xtv, l32, hf);
+            xs0 = tile_scores<T, DS>(smem + TileT::kBytes, xsv, l32, hf);
         }
-        bool active = wave_live;
-        if (CAUSAL) {
-            if (!DKMODE) active = active && (y0 <= min(n_q - 1, x0w + kTile - 1) + off);
-            else active = active && (y0 + kBN - 1 + off >= x0w);
-        }
-        if (active) {
-            f32x16 acct = {}, accs = {};
-            {
-                u32x4 yv[span_vecs<T, DT>()];
-                load_span_lds<T, DT, PT>(bt, l32, hf, yv);
-#pragma unroll
-                for (int ks = 0; ks < Ty<T>::ksteps(DT); ++ks)
-                    acct = Ty<T>::mma(Ty<T>::frag(yv, ks), Ty<T>::frag(xtv, ks), acct);
+        int sc = 0;  // stage holding tile it
+        auto step = [&](int it, f32x16 &cur_t, f32x16 &cur_s, f32x16 &nxt_t, f32x16 &nxt_s) {
+            const int sn = sc == 2 ? 0 : sc + 1, sw = sn == 2 ? 0 : sn + 1;
+            if (it + 2 < ntile) {
+                issue(it + 2, sw);
+                load_rows(it + 2);
             }
-            {
-                u32x4 yv[span_vecs<T, DS>()];
-                load_span_lds<T, DS, PS>(bs, l32, hf, yv);
+            const char *bn = smem + sn * STAGE;
+            const bool a_cur = active(it);
+            const bool a_nxt = it + 1 < ntile && active(it + 1);
+            const bool m_cur = need_mask(it);
+            if (a_cur && a_nxt && !m_cur) {
+                nxt_t = tile_scores<T, DT>(bn, xtv, l32, hf);
+                nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, xsv, l32, hf);
+                const int y0 = ystart + it * kBN;
+                float dsv[16];
+                tile_ds<false, CAUSAL, DKMODE>(cur_t, cur_s, ct, cs, nlt, nls, gts, &rowv[DKMODE ? sc : 0][0][0], y0,
+                                               hf, x, n_y, off, dsv);
+                if constexpr (sizeof(T) == 2) {
+                    constexpr int NM = Ty<T>::ksteps(DT) + Ty<T>::ksteps(DS);
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NM, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
 #pragma unroll
-                for (int ks = 0; ks < Ty<T>::ksteps(DS); ++ks)
-                    accs = Ty<T>::mma(Ty<T>::frag(yv, ks), Ty<T>::frag(xsv, ks), accs);
-            }
-            bool need_mask = y0 + kBN > n_y;
-            if (CAUSAL) {
-                if (!DKMODE) need_mask = need_mask || (y0 + kBN - 1 > x0w + off);
-                else need_mask = need_mask || (x0w + kTile - 1 > y0 + off);
-            }
-            // dS[y][x] = g * tau_s * (P_s - P_t), kept in fp32
-            float dsv[16];
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                f32x4 a_t, a_s, gg;
-                if (DKMODE) {
-                    const int r0 = grp * 8 + hf * 4;
-                    a_t = *reinterpret_cast<const f32x4 *>(rv + r0);
-                    a_s = *reinterpret_cast<const f32x4 *>(rv + kBN + r0);
-                    gg = *reinterpret_cast<const f32x4 *>(rv + 2 * kBN + r0);
-                } else {
-                    a_t = f32x4{nlt, nlt, nlt, nlt};
-                    a_s = f32x4{nls, nls, nls, nls};
-                    gg = f32x4{gts, gts, gts, gts};
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = grp * 4 + e;
-                    const float pt = fast_exp2(fmaf(acct[i], ct, a_t[e]));
-                    const float ps = fast_exp2(fmaf(accs[i], cs, a_s[e]));
-                    float d = gg[e] * (ps - pt);
-                    if (need_mask) {
-                        const int y = y0 + acc_row(i, hf);
-                        bool ok = y < n_y;
-                        if (CAUSAL) ok = ok && (DKMODE ? (x <= y + off) : (y <= x + off));
-                        d = ok ? d : 0.f;
-                    }
-                    dsv[i] = d;
-                }
-            }
-            // G^T[d][x] += Y_s^T[d][y] . dS[y][x]
-            if constexpr (sizeof(T) == 2) {
-                const int trow = 4 * hf + ((lane & 15) >> 2);
-                const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    bf16x8 bfrag;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bfrag[e] = (bf16_t)dsv[ks * 8 + e];
-#pragma unroll
-                    for (int t = 0; t < DS / kTile; ++t) {
-                        const char *a0 = bs + (16 * ks + trow) * PS + (t * kTile + tcol) * 2;
-                        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4 *)(a0));
-                        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4 *)(a0 + 8 * PS));
-                        const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0), b1 = __builtin_bit_cast(bf16x4, v1);
-                        const bf16x8 afrag = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                        G[t] = Ty<bf16_t>::mma(afrag, bfrag, G[t]);
+                    for (int k = 0; k < NM; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
                     }
                 }
+                tile_grad<T, DS>(G, dsv, smem + sc * STAGE + TileT::kBytes, lane, hf, l32);
             } else {
-#pragma unroll
-                for (int t = 0; t < DS / kTile; ++t) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float a = *reinterpret_cast<const float *>(bs + acc_row(i, hf) * PS + (t * kTile + l32) * 4);
-                        G[t] = Ty<float>::mma(a, dsv[i], G[t]);
-                    }
+                if (a_nxt) {
+                    nxt_t = tile_scores<T, DT>(bn, xtv, l32, hf);
+                    nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, xsv, l32, hf);
                 }
+                if (a_cur) ds_grad(cur_t, cur_s, it, sc, m_cur);
             }
+            if (it + 2 < ntile) store_rows(sw);
+            __syncthreads();
+            sc = sn;
+        };
+        for (int it = 0; it < ntile; it += 2) {
+            step(it, xt0, xs0, xt1, xs1);
+            if (it + 1 < ntile) step(it + 1, xt1, xs1, xt0, xs0);
         }
-        if (more) {
-            char *nt = smem + ((it + 1) & 1) * STAGE;
-            sgt.store(nt, tid);
-            sgs.store(nt + TILE_T, tid);
-            store_rows(nt);
+    } else {
+        for (int it = 0; it < ntile; ++it) {
+            const int sc = it & 1;
+            if (it + 1 < ntile) {
+                issue(it + 1, sc ^ 1);
+                load_rows(it + 1);
+            }
+            if (active(it)) {
+                const char *bc = smem + sc * STAGE;
+                const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
+                const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
+                ds_grad(cur_t, cur_s, it, sc, need_mask(it));
+            }
+            if (it + 1 < ntile) store_rows(sc ^ 1);
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     if (xv) {
