@@ -194,11 +194,16 @@ __device__ inline f32x16 tile_scores(const char *tile, const u32x4 *xv, int l32,
 
 // Online state of one query over the keys one half-wave sees.  Scores are kept
 // raw (x = q . k, unscaled); c = tau * log2(e) turns them into base-2 exponents.
+// The sums are relative to reference maxima mt, ms: the result is exact for any
+// reference that keeps the exponentials in range, so the reference is only
+// moved when a tile would push a sum past 2^64 (see online_step).
 struct Online {
-    float mt, lt, at, as;  // teacher: running max of x_t, sum e_t, sum e_t x_t, sum e_t x_s
-    float ms, ls;          // student: running max of x_s, sum e_s
+    float mt, lt, at, as;  // teacher: reference max of x_t, sum e_t, sum e_t x_t, sum e_t x_s
+    float ms, ls;          // student: reference max of x_s, sum e_s
 };
 
+// Exact update: the references become the running maxima and the sums are
+// rescaled to them.  Masked keys are excluded.
 template <bool MASK, bool CAUSAL>
 __device__ inline void online_update(Online &o, f32x16 xt, f32x16 xs, float ct, float cs, int k0, int hf, int q,
                                      int n_k, int off) {
@@ -243,6 +248,35 @@ __device__ inline void online_update(Online &o, f32x16 xt, f32x16 xs, float ct, 
     o.at = fmaf(o.at, rt, at);
     o.as = fmaf(o.as, rt, as);
     o.ls = fmaf(o.ls, rs, ls);
+}
+
+// Steady-state update of an unmasked tile: exponentials against the current
+// references, no maxima.  If any lane's tile sums are not safely below 2^64 (a
+// score grew far past the reference, the references are still unset, or the
+// row holds NaN), the whole wave redoes the tile with the exact update.
+template <bool CAUSAL>
+__device__ inline void online_step(Online &o, const f32x16 &xt, const f32x16 &xs, float ct, float cs, int k0, int hf,
+                                   int q, int n_k, int off) {
+    const float nmt = -ct * o.mt, nms = -cs * o.ms;
+    float lt = 0.f, ls = 0.f, at = 0.f, as = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float et = fast_exp2(fmaf(xt[i], ct, nmt));
+        const float es = fast_exp2(fmaf(xs[i], cs, nms));
+        lt += et;
+        ls += es;
+        at = fmaf(et, xt[i], at);
+        as = fmaf(et, xs[i], as);
+    }
+    const bool fine = (lt < 0x1p64f) && (ls < 0x1p64f);
+    if (__builtin_amdgcn_ballot_w64(!fine) != 0) {
+        online_update<false, CAUSAL>(o, xt, xs, ct, cs, k0, hf, q, n_k, off);
+    } else {
+        o.lt += lt;
+        o.ls += ls;
+        o.at += at;
+        o.as += as;
+    }
 }
 
 // One block = 4 waves x 32 queries.  The key tiles stream through a two-stage
@@ -314,7 +348,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
         if (a_cur && a_nxt && !m_cur) {
             nxt_t = tile_scores<T, DT>(bn, qtv, l32, hf);
             nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, qsv, l32, hf);
-            online_update<false, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
+            online_step<CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
             if constexpr (sizeof(T) == 2) {
                 constexpr int NM = Ty<T>::ksteps(DT) + Ty<T>::ksteps(DS);
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NM, 0);
@@ -332,7 +366,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
             }
             if (a_cur) {
                 if (m_cur) online_update<true, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
-                else online_update<false, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
+                else online_step<CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
             }
         }
         __syncthreads();
