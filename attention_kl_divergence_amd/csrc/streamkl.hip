@@ -515,32 +515,20 @@ __device__ inline void tile_grad(f32x16 *G, const float *dsv, const char *ys, in
     }
 }
 
-#ifndef STREAMKL_BWD_PIPE
-#define STREAMKL_BWD_PIPE 0
-#endif
-// PIPE: three-stage LDS ring, the scores of tile j+1 are issued interleaved
-// with dS of tile j (one wave per SIMD, ILP inside the wave).  Otherwise a
-// two-stage ring with tile-at-a-time work and two waves per SIMD overlapping
+// One (stationary block, head) of the backward: the kBlockX stationary items
+// x0 .. x0 + kBlockX - 1 (queries for dq_s, keys for dk_s) of head bh, with the
+// other kind streamed through a two-stage LDS ring.  Two waves per SIMD overlap
 // each other's MFMA and VALU phases.
-constexpr bool kBwdPipe = STREAMKL_BWD_PIPE != 0;
-
 template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE>
-__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && !kBwdPipe) ? 2 : 1) void streamkl_bwd_kernel(BwdParams p) {
+__device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams &p, int xb, int bh, char *smem,
+                                                                float (*rowv)[3][kBN]) {
     using TileT = Tile<T, DT>;
     using TileS = Tile<T, DS>;
-    constexpr int NSTAGE = kBwdPipe ? 3 : 2;
     constexpr int STAGE = TileT::kBytes + TileS::kBytes;
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
-    // dk mode: per-query -LSE_t log2 e, -LSE_s log2 e, g tau_s of each stage's rows
-    __shared__ __attribute__((aligned(16))) float rowv[DKMODE ? NSTAGE : 1][3][kBN];
 
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    // heaviest blocks first under a causal mask: high query blocks (dq) see the
-    // most keys, low key blocks (dk) are seen by the most queries
-    const int xb = DKMODE ? (wg % p.n_xblk) : (p.n_xblk - 1 - (wg % p.n_xblk));
-    const int bh = wg / p.n_xblk, hh = bh % p.H, bb = bh / p.H;
+    const int hh = bh % p.H, bb = bh / p.H;
     const T *Xt = static_cast<const T *>(p.x_t) + bb * p.st[0] + hh * p.st[1];
     const T *Xs = static_cast<const T *>(p.x_s) + bb * p.st[3] + hh * p.st[4];
     const T *Yt = static_cast<const T *>(p.y_t) + bb * p.st[6] + hh * p.st[7];
@@ -600,7 +588,6 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && !kBwdPipe) ? 2 : 1) vo
 
     issue(0, 0);
     load_rows(0);
-    if (kBwdPipe && ntile > 1) issue(1, 1);
 
     u32x4 xtv[span_vecs<T, DT>()], xsv[span_vecs<T, DS>()];
     load_span_global<T, DT>(Xt + (int64_t)xc * sxt, hf, xv, xtv);
@@ -619,10 +606,6 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && !kBwdPipe) ? 2 : 1) vo
     for (int t = 0; t < DS / kTile; ++t) G[t] = f32x16{};
 
     store_rows(0);
-    if (kBwdPipe && ntile > 1) {
-        load_rows(1);
-        store_rows(1);
-    }
     __syncthreads();
 
     auto ds_grad = [&](const f32x16 &cur_t, const f32x16 &cur_s, int it, int stage, bool m_cur) {
@@ -634,72 +617,20 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && !kBwdPipe) ? 2 : 1) vo
         tile_grad<T, DS>(G, dsv, smem + stage * STAGE + TileT::kBytes, lane, hf, l32);
     };
 
-    if constexpr (kBwdPipe) {
-        f32x16 xt0 = {}, xs0 = {}, xt1 = {}, xs1 = {};
-        if (active(0)) {
-            xt0 = tile_scores<T, DT>(smem, xtv, l32, hf);
-            xs0 = tile_scores<T, DS>(smem + TileT::kBytes, xsv, l32, hf);
+    for (int it = 0; it < ntile; ++it) {
+        const int sc = it & 1;
+        if (it + 1 < ntile) {
+            issue(it + 1, sc ^ 1);
+            load_rows(it + 1);
         }
-        int sc = 0;  // stage holding tile it
-        auto step = [&](int it, f32x16 &cur_t, f32x16 &cur_s, f32x16 &nxt_t, f32x16 &nxt_s) {
-            const int sn = sc == 2 ? 0 : sc + 1, sw = sn == 2 ? 0 : sn + 1;
-            if (it + 2 < ntile) {
-                issue(it + 2, sw);
-                load_rows(it + 2);
-            }
-            const char *bn = smem + sn * STAGE;
-            const bool a_cur = active(it);
-            const bool a_nxt = it + 1 < ntile && active(it + 1);
-            const bool m_cur = need_mask(it);
-            if (a_cur && a_nxt && !m_cur) {
-                nxt_t = tile_scores<T, DT>(bn, xtv, l32, hf);
-                nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, xsv, l32, hf);
-                const int y0 = ystart + it * kBN;
-                float dsv[16];
-                tile_ds<false, CAUSAL, DKMODE>(cur_t, cur_s, ct, cs, nlt, nls, gts, &rowv[DKMODE ? sc : 0][0][0], y0,
-                                               hf, x, n_y, off, dsv);
-                if constexpr (sizeof(T) == 2) {
-                    constexpr int NM = Ty<T>::ksteps(DT) + Ty<T>::ksteps(DS);
-                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NM, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
-#pragma unroll
-                    for (int k = 0; k < NM; ++k) {
-                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
-                    }
-                }
-                tile_grad<T, DS>(G, dsv, smem + sc * STAGE + TileT::kBytes, lane, hf, l32);
-            } else {
-                if (a_nxt) {
-                    nxt_t = tile_scores<T, DT>(bn, xtv, l32, hf);
-                    nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, xsv, l32, hf);
-                }
-                if (a_cur) ds_grad(cur_t, cur_s, it, sc, m_cur);
-            }
-            if (it + 2 < ntile) store_rows(sw);
-            __syncthreads();
-            sc = sn;
-        };
-        for (int it = 0; it < ntile; it += 2) {
-            step(it, xt0, xs0, xt1, xs1);
-            if (it + 1 < ntile) step(it + 1, xt1, xs1, xt0, xs0);
+        if (active(it)) {
+            const char *bc = smem + sc * STAGE;
+            const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
+            const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
+            ds_grad(cur_t, cur_s, it, sc, need_mask(it));
         }
-    } else {
-        for (int it = 0; it < ntile; ++it) {
-            const int sc = it & 1;
-            if (it + 1 < ntile) {
-                issue(it + 1, sc ^ 1);
-                load_rows(it + 1);
-            }
-            if (active(it)) {
-                const char *bc = smem + sc * STAGE;
-                const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
-                const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
-                ds_grad(cur_t, cur_s, it, sc, need_mask(it));
-            }
-            if (it + 1 < ntile) store_rows(sc ^ 1);
-            __syncthreads();
-        }
+        if (it + 1 < ntile) store_rows(sc ^ 1);
+        __syncthreads();
     }
 
     if (xv) {
@@ -722,6 +653,34 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && !kBwdPipe) ? 2 : 1) vo
     }
 }
 
+// One launch computes both gradients: per head, the query blocks (dq_s) and the
+// key blocks (dk_s) are interleaved in one work list, so every XCD gets both
+// kinds and the list of a head sits on one XCD (its tiles shared through that
+// L2).  Within a kind the heaviest blocks come first under a causal mask: high
+// query blocks see the most keys, low key blocks are seen by the most queries.
+template <typename T, int DT, int DS, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_bwd_kernel(BwdParams pq, BwdParams pk) {
+    constexpr int STAGE = Tile<T, DT>::kBytes + Tile<T, DS>::kBytes;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    // per-query -LSE_t log2 e, -LSE_s log2 e, g tau_s of each stage's rows (dk_s blocks)
+    __shared__ __attribute__((aligned(16))) float rowv[2][3][kBN];
+
+    const int nq = pq.n_xblk, nk = pk.n_xblk, m = min(nq, nk);
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = wg / (nq + nk), r = wg % (nq + nk);
+    bool dk;
+    int idx;
+    if (r < 2 * m) {
+        dk = (r & 1) == 0;
+        idx = r >> 1;
+    } else {
+        dk = nk > nq;
+        idx = m + (r - 2 * m);
+    }
+    if (dk) bwd_block<T, DT, DS, CAUSAL, true>(pk, idx, bh, smem, rowv);
+    else bwd_block<T, DT, DS, CAUSAL, false>(pq, nq - 1 - idx, bh, smem, rowv);
+}
+
 // ================================================================= host side
 struct Shape {
     int B, H, n_q, n_k, d_t, d_s;
@@ -738,9 +697,11 @@ streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, 
     if (causal && s.n_q > s.n_k) return STREAMKL_ERR_INVALID;
     if (!streamkl_supported(dtype, s.d_t, s.d_s)) return STREAMKL_ERR_UNSUPPORTED;
     const int64_t elt = dtype == STREAMKL_BF16 ? 2 : 4;
-    // grid size and 32-bit row arithmetic inside the kernels
+    // grid size (a dispatch holds at most 2^32 - 1 work-items; the backward
+    // grid has a block per query block and per key block of every head) and
+    // 32-bit row arithmetic inside the kernels
     const int64_t nblk_q = ((int64_t)s.n_q + kBlockX - 1) / kBlockX, nblk_k = ((int64_t)s.n_k + kBlockX - 1) / kBlockX;
-    if ((int64_t)s.B * s.H * (nblk_q > nblk_k ? nblk_q : nblk_k) > (int64_t)INT32_MAX) return STREAMKL_ERR_INVALID;
+    if ((int64_t)s.B * s.H * (nblk_q + nblk_k) * kThreads > (int64_t)UINT32_MAX) return STREAMKL_ERR_INVALID;
     if ((int64_t)s.n_q + kBlockX > (int64_t)INT32_MAX / 2 || (int64_t)s.n_k + kBlockX > (int64_t)INT32_MAX / 2)
         return STREAMKL_ERR_INVALID;
     const int dims[4] = {s.d_t, s.d_t, s.d_s, s.d_s};
@@ -765,15 +726,15 @@ streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, 
 }
 
 typedef void (*fwd_launch_t)(const FwdParams &, int grid, hipStream_t);
-typedef void (*bwd_launch_t)(const BwdParams &, int grid, hipStream_t);
+typedef void (*bwd_launch_t)(const BwdParams &, const BwdParams &, int grid, hipStream_t);
 
 template <typename T, int DT, int DS, bool C>
 void launch_fwd(const FwdParams &p, int grid, hipStream_t s) {
     hipLaunchKernelGGL((streamkl_fwd_kernel<T, DT, DS, C>), dim3(grid), dim3(kThreads), 0, s, p);
 }
-template <typename T, int DT, int DS, bool C, bool DK>
-void launch_bwd(const BwdParams &p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C, DK>), dim3(grid), dim3(kThreads), 0, s, p);
+template <typename T, int DT, int DS, bool C>
+void launch_bwd(const BwdParams &pq, const BwdParams &pk, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C>), dim3(grid), dim3(kThreads), 0, s, pq, pk);
 }
 
 template <typename T, int DT, int DS>
@@ -781,9 +742,8 @@ fwd_launch_t pick_fwd2(int causal) {
     return causal ? launch_fwd<T, DT, DS, true> : launch_fwd<T, DT, DS, false>;
 }
 template <typename T, int DT, int DS>
-bwd_launch_t pick_bwd2(int causal, bool dk) {
-    if (causal) return dk ? launch_bwd<T, DT, DS, true, true> : launch_bwd<T, DT, DS, true, false>;
-    return dk ? launch_bwd<T, DT, DS, false, true> : launch_bwd<T, DT, DS, false, false>;
+bwd_launch_t pick_bwd2(int causal) {
+    return causal ? launch_bwd<T, DT, DS, true> : launch_bwd<T, DT, DS, false>;
 }
 template <typename T>
 fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
@@ -794,11 +754,11 @@ fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
     return nullptr;
 }
 template <typename T>
-bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool dk) {
-    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal, dk);
-    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal, dk);
-    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal, dk);
-    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal, dk);
+bwd_launch_t pick_bwd1(int d_t, int d_s, int causal) {
+    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal);
+    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal);
+    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal);
+    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal);
     return nullptr;
 }
 
@@ -871,9 +831,11 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
     if (((uintptr_t)dq_s) % 16 != 0 || ((uintptr_t)dk_s) % 16 != 0) return STREAMKL_ERR_INVALID;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool bf = dtype == STREAMKL_BF16;
+    BwdParams pp[2];
     for (int pass = 0; pass < 2; ++pass) {
         const bool dk = pass == 1;
-        BwdParams p{};
+        BwdParams &p = pp[pass];
+        p = BwdParams{};
         // stationary operand first, streamed second
         const int xi = dk ? 1 : 0, yi = dk ? 0 : 1;  // 0 = queries, 1 = keys (index into q_t/k_t stride groups)
         const void *tq[2] = {q_t, k_t}, *sq[2] = {q_s, k_s};
@@ -891,11 +853,11 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
         p.tau_t = tau_t; p.tau_s = tau_s;
         p.lse_t = lse_t; p.lse_s = lse_s; p.g = grad_rows; p.g_scalar = grad_scalar;
         p.out = dk ? dk_s : dq_s;
-        bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal, dk) : pick_bwd1<float>(d_t, d_s, causal, dk);
-        if (!fn) return STREAMKL_ERR_UNSUPPORTED;
-        fn(p, B * H * p.n_xblk, hs);
-        if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
     }
+    bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal) : pick_bwd1<float>(d_t, d_s, causal);
+    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+    fn(pp[0], pp[1], B * H * (pp[0].n_xblk + pp[1].n_xblk), hs);
+    if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
     return STREAMKL_OK;
 }
 

@@ -11,10 +11,20 @@ Reported value: algorithmic fwd+bwd TFLOP/s over the timed steps, counting only
 the contractions over unmasked (query, key) pairs: forward 2 pairs (d_t + d_s),
 backward 2 pairs (d_t + 3 d_s) (the two score recomputes, dQ_s and dK_s).
 
+The roofline entry covers the dominant kernel, the backward (one launch holds
+both the dq_s and the dk_s blocks): achieved = its algorithmic flops per launch
+(2 (d_t + 3 d_s) per unmasked pair) over its mean duration from HIP events on
+the launch stream.  Its HBM traffic comes from a committed counter summary,
+profiles/streamkl_bwd_kernel.<workload>.traffic.txt, and is reported only while
+the kernel source still has the hash recorded there (else null).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-baseline-mem]
+                       [--no-cpu-baseline] [--no-baseline-mem] [--cpu-heads N]
+       python bench.py --copy-calibration MiB   (a plain device copy of known
+                       size, run under the same HBM byte counters to scale them)
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -66,30 +76,65 @@ def materialized_baseline_peak(w, d, torch):
         return None
 
 
-def cpu_baseline(w, x):
+def kernel_source_hash():
+    with open(os.path.join(ROOT, "attention_kl_divergence_amd", "csrc", "streamkl.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if the kernel
+    source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib, steps):
+    """A device-to-device copy of a known number of bytes, for scaling the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": steps}),
+          flush=True)
+
+
+def cpu_baseline(w, x, heads):
     """The fp64 oracle, as it stands, on a bounded slice of the same workload:
-    one head, the first 192 query rows against all N_K keys (full forward and
-    backward of that slice)."""
+    the first `heads` (batch, head) slices in full (every query row against
+    every key, forward and backward)."""
     import numpy as np
 
     import oracle
-    rows = min(w.n_q, 192)
-    sl = {k: np.ascontiguousarray(v[:1, :1, :rows] if k.startswith("q") else v[:1, :1], dtype=np.float64)
-          for k, v in x.items()}
-    if w.causal:  # keep the slice's rows at their bottom-right causal position
-        sl = {k: (np.ascontiguousarray(x[k][:1, :1, w.n_q - rows:], dtype=np.float64) if k.startswith("q") else v)
-              for k, v in sl.items()}
-    sw = w.resized(B=1, H=1, n_q=rows)
+    flat = {k: v.reshape((w.B * w.H,) + v.shape[2:]) for k, v in x.items()}
+    heads = max(1, min(heads, w.B * w.H))
+    sl = {k: np.ascontiguousarray(v[:heads][None], dtype=np.float64) for k, v in flat.items()}
+    sw = w.resized(B=1, H=heads)
     f, b = flops(sw)
     t0 = time.perf_counter()
     oracle.fwd(sl["q_t"], sl["k_t"], sl["q_s"], sl["k_s"], w.tau_t, w.tau_s, w.causal)
     oracle.bwd(sl["q_t"], sl["k_t"], sl["q_s"], sl["k_s"], w.tau_t, w.tau_s, w.causal)
     dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
-    return {"value": (f + b) / dt / 1e12, "unit": "TFLOP/s", "cores": int(os.environ.get("OMP_NUM_THREADS", cores)),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"fp64 oracle fwd+bwd, 1 head, {rows} query rows x {w.n_k} keys "
-                      f"({(f + b) / 1e9:.1f} GFLOP algorithmic)"}
+    return {"value": (f + b) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"fp64 oracle fwd+bwd of {heads} of the {w.B * w.H} (batch, head) slices in full "
+                      f"({w.n_q} query rows x {w.n_k} keys each, {(f + b) / 1e9:.1f} GFLOP algorithmic)"}
 
 
 def main():
@@ -100,12 +145,17 @@ def main():
     ap.add_argument("--workload", default="corr_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline-mem", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this primitive is measured on one GPU only; multi-GPU runs are not supported "
               "(the per-(batch, head) work shards with no exchange but is not built for several GPUs)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
 
     import numpy as np
     import torch
@@ -177,7 +227,11 @@ def main():
     print(f"[bench] fwd {np.mean(t_f):.3f} ms ({fwd_tf:.1f} TF/s), bwd {np.mean(t_b):.3f} ms ({bwd_tf:.1f} TF/s)",
           file=sys.stderr, flush=True)
 
+    # dominant kernel: the backward launch, unless the forward entry (forward
+    # kernel + the tiny sum kernel) takes longer
     dominant = "fwd" if np.mean(t_f) >= np.mean(t_b) else "bwd"
+    dom_kernel = "streamkl_fwd_kernel" if dominant == "fwd" else "streamkl_bwd_kernel"
+    dom_tf = fwd_tf if dominant == "fwd" else bwd_tf
     res = {
         "metric": "fused attn-KL fwd+bwd TFLOP/s & % bf16 MFMA peak at N=16K,d=128; extra HBM bytes",
         "value": round(value, 2),
@@ -198,17 +252,17 @@ def main():
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
         "extra_hbm_bytes": extra_bytes,
         "input_bytes": in_bytes,
-        "roofline": {"bound": "mfma", "kernel": f"streamkl_{dominant}",
-                     "achieved": round(fwd_tf if dominant == "fwd" else bwd_tf, 2), "peak": peak,
-                     "unit": "TFLOP/s",
-                     "frac": round((fwd_tf if dominant == "fwd" else bwd_tf) / peak, 4), "traffic": None},
+        "roofline": {"bound": "mfma", "kernel": dom_kernel, "achieved": round(dom_tf, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(dom_tf / peak, 4),
+                     "traffic": committed_traffic(dom_kernel, w.name),
+                     "ms_per_launch": round(float(np.mean(t_f if dominant == "fwd" else t_b)), 4)},
     }
     if not args.no_baseline_mem:
         bpk = materialized_baseline_peak(w, d, torch)
         res["materialized_baseline_peak_bytes"] = bpk
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded slice", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, x)
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
     print(json.dumps(res), flush=True)
 
 

@@ -53,7 +53,9 @@ extern "C" {
 
 typedef enum {
     STREAMKL_OK = 0,
-    STREAMKL_ERR_INVALID = 1,     /* null pointer, bad size, bad tau, misalignment, causal with n_q > n_k */
+    STREAMKL_ERR_INVALID = 1,     /* null pointer, bad size, bad tau, misalignment, causal with n_q > n_k,
+                                     or a problem too large for one dispatch (B H (ceil(n_q/128) +
+                                     ceil(n_k/128)) 256 >= 2^32, or n_q / n_k beyond 2^30 - 128) */
     STREAMKL_ERR_UNSUPPORTED = 2, /* (dtype, d_t, d_s) combination not built */
     STREAMKL_ERR_WORKSPACE = 3,   /* reserved: workspace too small */
     STREAMKL_ERR_HIP = 4          /* a HIP launch error was reported */
@@ -102,8 +104,9 @@ streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, 
  *                    grad_scalar for every row (1.0 for L = kl_sum)
  *   dq_s, dk_s       out, input dtype, contiguous
  *
- * No workspace is used: dq_s and dk_s come from two deterministic kernels
- * (query-major and key-major), with no atomics.
+ * No workspace is used: one deterministic launch, with no atomics, holds both a
+ * query-major block per 128 queries (dq_s) and a key-major block per 128 keys
+ * (dk_s) of every head.
  */
 streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
                              streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,

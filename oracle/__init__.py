@@ -46,6 +46,8 @@ def _load():
     lib.oracle_dq_rows.restype = None
     lib.oracle_dk_keys.argtypes = common + [ctypes.c_void_p, _D, _I, _I, _I, _i64p, _f64p]
     lib.oracle_dk_keys.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = _I
     _lib = lib
     return lib
 
@@ -132,3 +134,8 @@ def dk_keys(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, b, h, keys, g=None):
     lib.oracle_dk_keys(*arrs, B, H, n_q, n_k, d_t, d_s, float(tau_t), float(tau_s), int(causal),
                        gp, gs, int(b), int(h), keys.size, keys, out)
     return out
+
+
+def num_threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())

@@ -31,6 +31,7 @@
  * fp32 inputs are passed already widened, which is exact); outputs are fp64.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -354,4 +355,16 @@ void oracle_dk_keys(const double *q_t, const double *k_t, const double *q_s, con
         free(dS);
         free(part);
     }
+}
+
+/* Number of OpenMP threads the functions above run with (for reporting). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
 }
