@@ -30,8 +30,11 @@
 //    ds_read_b64_tr_b16, so no transposed copy is ever written.
 //  * Workgroups are renumbered so that the blocks of one (batch, head) land on
 //    the same XCD (the hardware deals workgroups round-robin over the 8 XCDs,
-//    each with its own L2); causal blocks are issued heaviest first.
+//    each with its own L2) and the heaviest blocks of every head are issued
+//    first (block_order).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -90,9 +93,36 @@ template <> struct Ty<float> {
 // 16-byte chunks in one half-wave span of a D-wide row
 template <typename T, int D> constexpr int span_vecs() { return D * Ty<T>::kBytes / 32; }
 
-__device__ inline int xcd_remap(int i, int n) {
-    const int x = i & 7, j = i >> 3, q = n >> 3, r = n & 7;
-    return x * q + min(x, r) + j;
+// Work order of a launch with `per_head` blocks for each of `nheads` heads,
+// ranked 0 (heaviest) .. per_head - 1 within a head.  The hardware deals
+// workgroups round-robin over the 8 XCDs (block id b goes to XCD b % 8 as its
+// (b / 8)-th block), each XCD with its own L2.  The heads are split over the
+// XCDs so that all of a head's tiles go through one L2.  Head-major walks one
+// head after the other, which keeps the blocks in flight on an XCD on as few
+// heads as possible (their streamed tiles are shared in L2).  Rank-major walks
+// the heaviest rank of every head of the XCD first; the host picks it when
+// single blocks are long next to the whole launch, where head-major would
+// start the heavy blocks of the last heads too late.
+__device__ inline void block_order(int bid, int nblocks, int nheads, int per_head, bool rank_major, int &head,
+                                   int &rank) {
+    if ((nheads & 7) == 0) {
+        const int hx = nheads >> 3, x = bid & 7, j = bid >> 3;
+        if (rank_major) {
+            rank = j / hx;
+            head = x * hx + j % hx;
+        } else {
+            head = x * hx + j / per_head;
+            rank = j % per_head;
+        }
+    } else if (rank_major) {
+        rank = bid / nheads;
+        head = bid % nheads;
+    } else {
+        const int x = bid & 7, j = bid >> 3, q = nblocks >> 3, r = nblocks & 7;
+        const int wg = x * q + min(x, r) + j;  // contiguous block ranges per XCD
+        head = wg / per_head;
+        rank = wg % per_head;
+    }
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -172,7 +202,8 @@ __device__ inline int acc_row(int i, int h) { return (i >> 2) * 8 + h * 4 + (i &
 struct FwdParams {
     const void *q_t, *k_t, *q_s, *k_s;
     int64_t st[12];  // q_t(b,h,n), k_t(b,h,n), q_s(b,h,n), k_s(b,h,n), in elements
-    int H, n_q, n_k, n_qblk;
+    int H, nheads, n_q, n_k, n_qblk;
+    bool rank_major;
     float tau_t, tau_s;
     float *kl, *lse_t, *lse_s;
 };
@@ -292,9 +323,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
 
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int qb = p.n_qblk - 1 - (wg % p.n_qblk);
-    const int bh = wg / p.n_qblk, hh = bh % p.H, bb = bh / p.H;
+    int bh, rank;
+    block_order(blockIdx.x, gridDim.x, p.nheads, p.n_qblk, p.rank_major, bh, rank);
+    const int qb = p.n_qblk - 1 - rank;  // high query blocks see the most keys under a causal mask
+    const int hh = bh % p.H, bb = bh / p.H;
     const T *Qt = static_cast<const T *>(p.q_t) + bb * p.st[0] + hh * p.st[1];
     const T *Kt = static_cast<const T *>(p.k_t) + bb * p.st[3] + hh * p.st[4];
     const T *Qs = static_cast<const T *>(p.q_s) + bb * p.st[6] + hh * p.st[7];
@@ -431,12 +463,34 @@ __global__ __launch_bounds__(1024) void streamkl_sum_kernel(const float *x, int6
 struct BwdParams {
     const void *x_t, *x_s, *y_t, *y_s;
     int64_t st[12];  // x_t(b,h,n), x_s(b,h,n), y_t(b,h,n), y_s(b,h,n)
-    int H, n_x, n_y, n_q, n_k, n_xblk;
+    int H, nheads, n_x, n_y, n_q, n_k, n_xblk;
+    bool rank_major;
     float tau_t, tau_s;
     const float *lse_t, *lse_s, *g;
     float g_scalar;
     void *out;
 };
+
+// Range [ystart, yend) of streamed rows that stationary block xb meets: all of
+// them, or under a causal mask (key j allowed for query i iff j <= i + n_k - n_q)
+// the keys up to the block's last query (dq_s), the queries from the block's
+// first key on, rounded down to a tile (dk_s).
+template <bool CAUSAL, bool DKMODE>
+__device__ inline void bwd_range(const BwdParams &p, int xb, int &ystart, int &yend) {
+    const int off = p.n_k - p.n_q;
+    ystart = 0;
+    yend = p.n_y;
+    if (CAUSAL) {
+        if (!DKMODE) yend = min(p.n_k, min(p.n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
+        else ystart = (max(0, xb * kBlockX - off) / kBN) * kBN;
+    }
+}
+template <bool CAUSAL, bool DKMODE>
+__device__ inline int bwd_tiles(const BwdParams &p, int xb) {
+    int ys, ye;
+    bwd_range<CAUSAL, DKMODE>(p, xb, ys, ye);
+    return (ye - ys + kBN - 1) / kBN;
+}
 
 // dS[y][x] = g * tau_s * (P_s - P_t) for one 32x32 tile, in fp32, with
 // P = 2^(x * c - LSE * log2 e).  Per-query values (-LSE_t log2 e, -LSE_s log2 e,
@@ -543,11 +597,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     const int xc = xv ? x : n_x - 1;
     const bool wave_live = x0w < n_x;
 
-    int ystart = 0, yend = n_y;
-    if (CAUSAL) {
-        if (!DKMODE) yend = min(p.n_k, min(n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
-        else ystart = (max(0, xb * kBlockX - off) / kBN) * kBN;
-    }
+    int ystart, yend;
+    bwd_range<CAUSAL, DKMODE>(p, xb, ystart, yend);
     const int ntile = (yend - ystart + kBN - 1) / kBN;
     auto active = [&](int t) {
         const int y0 = ystart + t * kBN;
@@ -653,11 +704,11 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     }
 }
 
-// One launch computes both gradients: per head, the query blocks (dq_s) and the
-// key blocks (dk_s) are interleaved in one work list, so every XCD gets both
-// kinds and the list of a head sits on one XCD (its tiles shared through that
-// L2).  Within a kind the heaviest blocks come first under a causal mask: high
-// query blocks see the most keys, low key blocks are seen by the most queries.
+// One launch computes both gradients: each head has one work list holding its
+// query blocks (dq_s) and its key blocks (dk_s), heaviest first (under a causal
+// mask high query blocks see the most keys and low key blocks are seen by the
+// most queries; for rectangular shapes the kind with the longer stream goes
+// first), walked in the order of block_order.
 template <typename T, int DT, int DS, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_bwd_kernel(BwdParams pq, BwdParams pk) {
     constexpr int STAGE = Tile<T, DT>::kBytes + Tile<T, DS>::kBytes;
@@ -665,20 +716,29 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_bwd
     // per-query -LSE_t log2 e, -LSE_s log2 e, g tau_s of each stage's rows (dk_s blocks)
     __shared__ __attribute__((aligned(16))) float rowv[2][3][kBN];
 
-    const int nq = pq.n_xblk, nk = pk.n_xblk, m = min(nq, nk);
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / (nq + nk), r = wg % (nq + nk);
-    bool dk;
-    int idx;
-    if (r < 2 * m) {
-        dk = (r & 1) == 0;
-        idx = r >> 1;
-    } else {
-        dk = nk > nq;
-        idx = m + (r - 2 * m);
+    int bh, r;
+    block_order(blockIdx.x, gridDim.x, pq.nheads, pq.n_xblk + pk.n_xblk, pq.rank_major, bh, r);
+    // Rank r of a head's list: query blocks heaviest first (A, index i -> block
+    // nq - 1 - i) merged with key blocks heaviest first (B, index j -> block j)
+    // by streamed-tile count, ties alternating.  Both lists are non-increasing,
+    // so the A count among the first r entries is found by bisection.
+    const int nq = pq.n_xblk, nk = pk.n_xblk;
+    auto wa = [&](int i) { return bwd_tiles<CAUSAL, false>(pq, nq - 1 - i); };
+    auto wb = [&](int j) { return bwd_tiles<CAUSAL, true>(pk, j); };
+    auto a_first = [&](int i, int j) {
+        const int x = wa(i), y = wb(j);
+        return x > y || (x == y && i <= j);
+    };
+    int lo = max(0, r - nk), hi = min(r, nq);
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a_first(mid, r - 1 - mid)) lo = mid + 1;
+        else hi = mid;
     }
+    const bool dk = !(r - lo >= nk || (lo < nq && a_first(lo, r - lo)));
+    const int idx = dk ? r - lo : nq - 1 - lo;
     if (dk) bwd_block<T, DT, DS, CAUSAL, true>(pk, idx, bh, smem, rowv);
-    else bwd_block<T, DT, DS, CAUSAL, false>(pq, nq - 1 - idx, bh, smem, rowv);
+    else bwd_block<T, DT, DS, CAUSAL, false>(pq, idx, bh, smem, rowv);
 }
 
 // ================================================================= host side
@@ -723,6 +783,31 @@ streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, 
             if ((st[3 * t + k] * elt) % 16 != 0) return STREAMKL_ERR_INVALID;
     }
     return STREAMKL_OK;
+}
+
+// Streamed tiles of each block (the same formulas as the kernels' ranges).
+int64_t fwd_block_tiles(const Shape &s, int causal, int qb) {
+    const int off = s.n_k - s.n_q;
+    const int qlast = std::min(s.n_q - 1, qb * kBlockX + kBlockX - 1);
+    const int kend = causal ? std::min(s.n_k, qlast + off + 1) : s.n_k;
+    return (kend + kBN - 1) / kBN;
+}
+int64_t bwd_block_tiles(const Shape &s, int causal, bool dk, int xb) {
+    const int off = s.n_k - s.n_q;
+    int ys = 0, ye = dk ? s.n_q : s.n_k;
+    if (causal) {
+        if (!dk) ye = std::min(s.n_k, std::min(s.n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
+        else ys = (std::max(0, xb * kBlockX - off) / kBN) * kBN;
+    }
+    return (ye - ys + kBN - 1) / kBN;
+}
+// Rank-major order when block lengths differ and the longest block is more
+// than a quarter of what one workgroup slot of an XCD runs over the whole
+// launch (32 CUs x 2 workgroups).  Equal blocks balance in either order and
+// keep the head-major order for its L2 reuse.
+bool want_rank_major(int64_t min_tiles, int64_t max_tiles, int64_t head_tiles, int64_t nheads) {
+    const int64_t heads_per_xcd = (nheads + 7) / 8;
+    return 2 * max_tiles > 3 * min_tiles && 4 * max_tiles > heads_per_xcd * head_tiles / 64;
 }
 
 typedef void (*fwd_launch_t)(const FwdParams &, int grid, hipStream_t);
@@ -799,8 +884,18 @@ streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, 
     if (rc != STREAMKL_OK) return rc;
     if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
     p.q_t = q_t; p.k_t = k_t; p.q_s = q_s; p.k_s = k_s;
-    p.H = H; p.n_q = n_q; p.n_k = n_k;
+    p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
     p.n_qblk = (n_q + kBlockX - 1) / kBlockX;
+    {
+        int64_t mn = INT64_MAX, mx = 0, tot = 0;
+        for (int qb = 0; qb < p.n_qblk; ++qb) {
+            const int64_t t = fwd_block_tiles(s, causal, qb);
+            mn = std::min(mn, t);
+            mx = std::max(mx, t);
+            tot += t;
+        }
+        p.rank_major = want_rank_major(mn, mx, tot, p.nheads);
+    }
     p.tau_t = tau_t; p.tau_s = tau_s;
     p.kl = kl_rows; p.lse_t = lse_t; p.lse_s = lse_s;
     fwd_launch_t fn = dtype == STREAMKL_BF16 ? pick_fwd1<bf16_t>(d_t, d_s, causal) : pick_fwd1<float>(d_t, d_s, causal);
@@ -846,13 +941,24 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
             p.st[6 + k] = st[3 * yi + k];
             p.st[9 + k] = st[3 * (2 + yi) + k];
         }
-        p.H = H; p.n_q = n_q; p.n_k = n_k;
+        p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
         p.n_x = dk ? n_k : n_q;
         p.n_y = dk ? n_q : n_k;
         p.n_xblk = (p.n_x + kBlockX - 1) / kBlockX;
         p.tau_t = tau_t; p.tau_s = tau_s;
         p.lse_t = lse_t; p.lse_s = lse_s; p.g = grad_rows; p.g_scalar = grad_scalar;
         p.out = dk ? dk_s : dq_s;
+    }
+    {
+        int64_t mn = INT64_MAX, mx = 0, tot = 0;
+        for (int pass = 0; pass < 2; ++pass)
+            for (int xb = 0; xb < pp[pass].n_xblk; ++xb) {
+                const int64_t t = bwd_block_tiles(s, causal, pass == 1, xb);
+                mn = std::min(mn, t);
+                mx = std::max(mx, t);
+                tot += t;
+            }
+        pp[0].rank_major = pp[1].rank_major = want_rank_major(mn, mx, tot, (int64_t)B * H);
     }
     bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal) : pick_bwd1<float>(d_t, d_s, causal);
     if (!fn) return STREAMKL_ERR_UNSUPPORTED;
