@@ -83,6 +83,8 @@ INV, UNS = skl.STREAMKL_ERR_INVALID, skl.STREAMKL_ERR_UNSUPPORTED
     (dict(strides=[3 * 100 * 128, 100 * 128, 120] + [0, 0, 128] * 3), INV),  # 120 bf16 = 240 B ok, k_t b/h 0 ok ...
     (dict(strides=[3 * 100 * 128, 100 * 128, 100] + [0, 0, 128] * 3), INV),  # row stride < d_t
     (dict(strides=[3 * 100 * 128, 100 * 128, 132] + [0, 0, 128] * 3), INV),  # 264 B rows, not 16-B aligned
+    (dict(B=1024, H=1024, n_q=4096, n_k=4096), INV),  # 2^20 heads x 64 blocks x 256 threads >= 2^32 work-items
+    (dict(n_q=(1 << 30), n_k=(1 << 30), B=1, H=1), INV),  # row indices beyond 32-bit kernel arithmetic
 ])
 def test_fwd_rejects_bad_arguments_before_any_hip_call(kw, code):
     assert fwd(**kw) == code
@@ -96,6 +98,7 @@ def test_bwd_rejects_bad_arguments_before_any_hip_call():
     assert bwd(causal=1) == INV
     assert bwd(d_s=80) == UNS
     assert bwd(tau_s=-1.0) == INV
+    assert bwd(B=1024, H=1024, n_q=4096, n_k=4096) == INV
 
 
 def test_python_binding_fails_loudly_without_device_tensors():
