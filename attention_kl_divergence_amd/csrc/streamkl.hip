@@ -90,6 +90,15 @@ template <> struct Ty<float> {
     static constexpr int ksteps(int D) { return D / 2; }
 };
 
+// Barrier that publishes tiles filled by direct global->LDS loads.  Those loads
+// count on the wave's vmcnt, and a workgroup barrier alone does not wait for
+// them, so every wave first drains its own loads (vmcnt(0), lgkmcnt(0)); after
+// the barrier every wave's share of the tiles is in LDS.
+__device__ inline void dma_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __syncthreads();
+}
+
 // 16-byte chunks in one half-wave span of a D-wide row
 template <typename T, int D> constexpr int span_vecs() { return D * Ty<T>::kBytes / 32; }
 
@@ -361,13 +370,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
     const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
     Online o{kMasked, 0.f, 0.f, 0.f, kMasked, 0.f};
 
-    __syncthreads();
+    dma_barrier();
     f32x16 xt0 = {}, xs0 = {}, xt1 = {}, xs1 = {};
     if (active(0)) {
         xt0 = tile_scores<T, DT>(smem, qtv, l32, hf);
         xs0 = tile_scores<T, DS>(smem + TileT::kBytes, qsv, l32, hf);
     }
-    __syncthreads();  // every wave is done with stage 0 before tile 2 lands there
+    dma_barrier();  // every wave is done with stage 0 before tile 2 lands there
 
     // softmax of tile `it` (registers cur_*) + scores of tile it+1 (into nxt_*)
     auto step = [&](int it, f32x16 &cur_t, f32x16 &cur_s, f32x16 &nxt_t, f32x16 &nxt_s) {
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd
                 else online_step<CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
             }
         }
-        __syncthreads();
+        dma_barrier();  // publishes tile it + 2 for the next step's scores
     };
     for (int it = 0; it < ntile; it += 2) {
         step(it, xt0, xs0, xt1, xs1);
@@ -496,7 +505,7 @@ __device__ inline int bwd_tiles(const BwdParams &p, int xb) {
 // P = 2^(x * c - LSE * log2 e).  Per-query values (-LSE_t log2 e, -LSE_s log2 e,
 // g tau_s) are per lane when the queries are the stationary items, else they
 // come from the stage's LDS row-value block rv[3][kBN].
-template <bool MASK, bool CAUSAL, bool DKMODE>
+template <bool MASK, bool CAUSAL, bool DKMODE, int RS = kBN>
 __device__ inline void tile_ds(const f32x16 &xt, const f32x16 &xs, float ct, float cs, float nlt, float nls,
                                float gts, const float *rv, int y0, int hf, int x, int n_y, int off, float *dsv) {
 #pragma unroll
@@ -505,8 +514,8 @@ __device__ inline void tile_ds(const f32x16 &xt, const f32x16 &xs, float ct, flo
         if (DKMODE) {
             const int r0 = grp * 8 + hf * 4;
             a_t = *reinterpret_cast<const f32x4 *>(rv + r0);
-            a_s = *reinterpret_cast<const f32x4 *>(rv + kBN + r0);
-            gg = *reinterpret_cast<const f32x4 *>(rv + 2 * kBN + r0);
+            a_s = *reinterpret_cast<const f32x4 *>(rv + RS + r0);
+            gg = *reinterpret_cast<const f32x4 *>(rv + 2 * RS + r0);
         } else {
             a_t = f32x4{nlt, nlt, nlt, nlt};
             a_s = f32x4{nls, nls, nls, nls};
@@ -569,16 +578,25 @@ __device__ inline void tile_grad(f32x16 *G, const float *dsv, const char *ys, in
     }
 }
 
+#ifndef STREAMKL_BWD_SUB
+#define STREAMKL_BWD_SUB 2
+#endif
+// Streamed rows per pipeline stage of the backward: kBwdSub 32-row tiles
+// share one barrier and one round of loads.
+constexpr int kBwdSub = STREAMKL_BWD_SUB;
+constexpr int kBwdRows = kBwdSub * kBN;
+
 // One (stationary block, head) of the backward: the kBlockX stationary items
 // x0 .. x0 + kBlockX - 1 (queries for dq_s, keys for dk_s) of head bh, with the
 // other kind streamed through a two-stage LDS ring.  Two waves per SIMD overlap
 // each other's MFMA and VALU phases.
 template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE>
 __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams &p, int xb, int bh, char *smem,
-                                                                float (*rowv)[3][kBN]) {
+                                                                float (*rowv)[3][kBwdRows]) {
     using TileT = Tile<T, DT>;
     using TileS = Tile<T, DS>;
-    constexpr int STAGE = TileT::kBytes + TileS::kBytes;
+    constexpr int PAIR = TileT::kBytes + TileS::kBytes;  // one 32-row tile of both tensors
+    constexpr int STAGE = kBwdSub * PAIR;
 
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -612,15 +630,22 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         if (CAUSAL) m = m || (DKMODE ? (x0w + kTile - 1 > y0 + off) : (y0 + kBN - 1 > x0w + off));
         return m;
     };
-    auto issue = [&](int t, int stage) {
-        char *base = smem + stage * STAGE;
-        dma_tile<T, DT>(Yt, syt, ystart + t * kBN, n_y, base, w, lane);
-        dma_tile<T, DS>(Ys, sys, ystart + t * kBN, n_y, base + TileT::kBytes, w, lane);
+    const int nstage = (ntile + kBwdSub - 1) / kBwdSub;
+    auto issue = [&](int st, int stage) {
+#pragma unroll
+        for (int sub = 0; sub < kBwdSub; ++sub) {
+            const int t = st * kBwdSub + sub;
+            if (t < ntile) {
+                char *base = smem + stage * STAGE + sub * PAIR;
+                dma_tile<T, DT>(Yt, syt, ystart + t * kBN, n_y, base, w, lane);
+                dma_tile<T, DS>(Ys, sys, ystart + t * kBN, n_y, base + TileT::kBytes, w, lane);
+            }
+        }
     };
-    float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query y0 + tid (tid < kBN)
-    auto load_rows = [&](int t) {
-        if (DKMODE && tid < kBN) {
-            const int y = ystart + t * kBN + tid;
+    float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query y0 + tid (tid < kBwdRows)
+    auto load_rows = [&](int st) {
+        if (DKMODE && tid < kBwdRows) {
+            const int y = ystart + st * kBwdRows + tid;
             rv0 = rv1 = rv2 = 0.f;
             if (y < n_q) {
                 rv0 = -p.lse_t[rowbase + y] * kLog2e;
@@ -630,7 +655,7 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         }
     };
     auto store_rows = [&](int stage) {
-        if (DKMODE && tid < kBN) {
+        if (DKMODE && tid < kBwdRows) {
             rowv[stage][0][tid] = rv0;
             rowv[stage][1][tid] = rv1;
             rowv[stage][2][tid] = rv2;
@@ -657,31 +682,37 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     for (int t = 0; t < DS / kTile; ++t) G[t] = f32x16{};
 
     store_rows(0);
-    __syncthreads();
+    dma_barrier();
 
-    auto ds_grad = [&](const f32x16 &cur_t, const f32x16 &cur_s, int it, int stage, bool m_cur) {
+    auto ds_grad = [&](const f32x16 &cur_t, const f32x16 &cur_s, int it, int stage, int sub, bool m_cur) {
         const int y0 = ystart + it * kBN;
-        const float *rv = &rowv[DKMODE ? stage : 0][0][0];
+        const float *rv = &rowv[DKMODE ? stage : 0][0][DKMODE ? sub * kBN : 0];
         float dsv[16];
-        if (m_cur) tile_ds<true, CAUSAL, DKMODE>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
-        else tile_ds<false, CAUSAL, DKMODE>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
-        tile_grad<T, DS>(G, dsv, smem + stage * STAGE + TileT::kBytes, lane, hf, l32);
+        if (m_cur)
+            tile_ds<true, CAUSAL, DKMODE, kBwdRows>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
+        else
+            tile_ds<false, CAUSAL, DKMODE, kBwdRows>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
+        tile_grad<T, DS>(G, dsv, smem + stage * STAGE + sub * PAIR + TileT::kBytes, lane, hf, l32);
     };
 
-    for (int it = 0; it < ntile; ++it) {
-        const int sc = it & 1;
-        if (it + 1 < ntile) {
-            issue(it + 1, sc ^ 1);
-            load_rows(it + 1);
+    for (int st = 0; st < nstage; ++st) {
+        const int sc = st & 1;
+        if (st + 1 < nstage) {
+            issue(st + 1, sc ^ 1);
+            load_rows(st + 1);
         }
-        if (active(it)) {
-            const char *bc = smem + sc * STAGE;
-            const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
-            const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
-            ds_grad(cur_t, cur_s, it, sc, need_mask(it));
+#pragma unroll
+        for (int sub = 0; sub < kBwdSub; ++sub) {
+            const int it = st * kBwdSub + sub;
+            if (it < ntile && active(it)) {
+                const char *bc = smem + sc * STAGE + sub * PAIR;
+                const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
+                const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
+                ds_grad(cur_t, cur_s, it, sc, sub, need_mask(it));
+            }
         }
-        if (it + 1 < ntile) store_rows(sc ^ 1);
-        __syncthreads();
+        if (st + 1 < nstage) store_rows(sc ^ 1);
+        dma_barrier();
     }
 
     if (xv) {
@@ -711,10 +742,10 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 // first), walked in the order of block_order.
 template <typename T, int DT, int DS, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_bwd_kernel(BwdParams pq, BwdParams pk) {
-    constexpr int STAGE = Tile<T, DT>::kBytes + Tile<T, DS>::kBytes;
+    constexpr int STAGE = kBwdSub * (Tile<T, DT>::kBytes + Tile<T, DS>::kBytes);
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
     // per-query -LSE_t log2 e, -LSE_s log2 e, g tau_s of each stage's rows (dk_s blocks)
-    __shared__ __attribute__((aligned(16))) float rowv[2][3][kBN];
+    __shared__ __attribute__((aligned(16))) float rowv[2][3][kBwdRows];
 
     int bh, r;
     block_order(blockIdx.x, gridDim.x, pq.nheads, pq.n_xblk + pk.n_xblk, pq.rank_major, bh, r);

@@ -1,0 +1,64 @@
+"""Properties of the generated gfx950 code that the kernels' correctness rests on
+(CPU only: the device code is compiled to assembly here, nothing runs).
+
+Streamed tiles are written into LDS by direct global->LDS loads, which count on
+the issuing wave's vmcnt.  A workgroup barrier does not wait for them by
+itself, so every s_barrier in the forward and backward kernels must directly
+follow an s_waitcnt that drains vmcnt; otherwise a wave could pass the barrier
+with its share of a tile still in flight and other waves would read stale LDS.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from attention_kl_divergence_amd import build as hip_build
+
+HIPCC = hip_build.HIPCC
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "streamkl.s"
+    flags = [f for f in hip_build.FLAGS if f not in ("-shared",)]
+    res = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), hip_build.SRC],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return out.read_text().split("\n")
+
+
+def _kernels(lines):
+    starts = [(i, l.split(":")[0]) for i, l in enumerate(lines)
+              if re.match(r"^_ZN12_GLOBAL__N_1\d+streamkl_(fwd|bwd)_kernel\w*:", l)]
+    for i, name in starts:
+        end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
+        yield name, lines[i:end]
+
+
+def test_every_kernel_barrier_drains_vmcnt_first(asm):
+    kernels = list(_kernels(asm))
+    assert len(kernels) == 32  # {bf16, f32} x {64, 128}^2 x {causal, not} for each of fwd and bwd
+    for name, body in kernels:
+        nbar = 0
+        for k, line in enumerate(body):
+            if line.strip().startswith("s_barrier"):
+                nbar += 1
+                j = k - 1
+                while body[j].strip().startswith(";") or not body[j].strip() or body[j].startswith("."):
+                    j -= 1
+                assert "s_waitcnt" in body[j] and "vmcnt(0)" in body[j], f"{name}: barrier at +{k} after {body[j]!r}"
+        assert nbar >= 2, name
+
+
+def test_no_scratch_in_kernels(asm):
+    """Register spills to scratch would make the hot loops memory-bound."""
+    text = "\n".join(asm)
+    found = list(re.finditer(r"\.name:\s+(_ZN12_GLOBAL__N_1\d+streamkl_\w+)[\s\S]*?"
+                             r"\.private_segment_fixed_size:\s+(\d+)", text))
+    assert len(found) == 33  # 32 forward/backward instantiations + the sum kernel
+    for m in found:
+        assert int(m.group(2)) == 0, m.group(1)
