@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 
@@ -57,8 +58,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // running max of a lane that has seen no allowed key yet stays finite.
 constexpr float kMasked = -1.0e30f;
 
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kWaves = 4;
+#ifndef STREAMKL_WAVES
+#define STREAMKL_WAVES 4
+#endif
+constexpr int kWaves = STREAMKL_WAVES;  // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+// workgroups per CU the bf16 kernels are built for: two waves per SIMD
+constexpr int kBf16Blocks = 8 / kWaves;
 constexpr int kTile = 32;      // MFMA tile edge; each wave owns 32 stationary items
 constexpr int kBlockX = kWaves * kTile;
 constexpr int kBN = 32;        // streamed rows per pipeline stage
@@ -165,12 +171,13 @@ struct Tile {
 template <typename T, int D>
 __device__ inline void dma_tile(const T *base, int64_t stride_n, int row0, int nrows, char *tile, int wv, int lane) {
     using L = Tile<T, D>;
-    static_assert(L::kBytes % (1024 * kWaves) == 0, "tile must split evenly over the waves");
-    constexpr int kPerWave = L::kBytes / 1024 / kWaves;
+    constexpr int kSlots = L::kBytes / 1024;  // 1 KiB per wave instruction
+    constexpr int kPerWave = (kSlots + kWaves - 1) / kWaves;
 #pragma unroll
     for (int k = 0; k < kPerWave; ++k) {
-        const int slot = wv * kPerWave + k;  // wave-uniform
-        const int pos = slot * 64 + lane;    // chunk slot this lane fills
+        const int slot = k * kWaves + wv;  // wave-uniform
+        if (kSlots % kWaves != 0 && slot >= kSlots) break;
+        const int pos = slot * 64 + lane;  // chunk slot this lane fills
         const int r = pos / L::kChunks;
         const int c = (pos % L::kChunks) ^ L::swz(r);
         int gr = row0 + r;
@@ -319,12 +326,12 @@ __device__ inline void online_step(Online &o, const f32x16 &xt, const f32x16 &xs
     }
 }
 
-// One block = 4 waves x 32 queries.  The key tiles stream through a two-stage
+// One block = kWaves waves x 32 queries.  The key tiles stream through a two-stage
 // LDS ring filled by direct global->LDS loads; in steady state the MFMAs of
 // tile j+1 are issued interleaved with the exponentials and sums of tile j
 // (which only need registers) while the loads of tile j+2 are in flight.
 template <typename T, int DT, int DS, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void streamkl_fwd_kernel(FwdParams p) {
     using TileT = Tile<T, DT>;
     using TileS = Tile<T, DS>;
     constexpr int STAGE = TileT::kBytes + TileS::kBytes;
@@ -695,7 +702,12 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         tile_grad<T, DS>(G, dsv, smem + stage * STAGE + sub * PAIR + TileT::kBytes, lane, hf, l32);
     };
 
-    for (int st = 0; st < nstage; ++st) {
+    // One ring stage: loads for the next stage, the tiles of this one, barrier.
+    // PLAIN stages hold only tiles that are active and unmasked for this wave,
+    // so their body has no branches (branches around the MFMA chain make the
+    // compiler copy the gradient accumulators at every join).
+    auto stage_body = [&](int st, auto plain_tag) {
+        constexpr bool PLAIN = decltype(plain_tag)::value;
         const int sc = st & 1;
         if (st + 1 < nstage) {
             issue(st + 1, sc ^ 1);
@@ -704,8 +716,12 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 #pragma unroll
         for (int sub = 0; sub < kBwdSub; ++sub) {
             const int it = st * kBwdSub + sub;
-            if (it < ntile && active(it)) {
-                const char *bc = smem + sc * STAGE + sub * PAIR;
+            const char *bc = smem + sc * STAGE + sub * PAIR;
+            if (PLAIN) {
+                const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
+                const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
+                ds_grad(cur_t, cur_s, it, sc, sub, false);
+            } else if (it < ntile && active(it)) {
                 const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
                 const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
                 ds_grad(cur_t, cur_s, it, sc, sub, need_mask(it));
@@ -713,7 +729,28 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         }
         if (st + 1 < nstage) store_rows(sc ^ 1);
         dma_barrier();
+    };
+    // This wave's plain tiles are [t_lo, t_hi): tiles wholly inside the
+    // streamed range and, under a causal mask, wholly on the allowed side.
+    int t_lo = 0, t_hi = 0;
+    if (wave_live) {
+        t_hi = (n_y - ystart) / kBN;  // full tiles
+        if (CAUSAL && !DKMODE) {
+            // y0 + kBN - 1 <= x0w + off
+            const int lim = x0w + off - (kBN - 1) - ystart;
+            t_hi = min(t_hi, lim < 0 ? 0 : lim / kBN + 1);
+        }
+        if (CAUSAL && DKMODE) {
+            // y0 >= x0w + kTile - 1 - off
+            const int need = x0w + kTile - 1 - off - ystart;
+            t_lo = need <= 0 ? 0 : (need + kBN - 1) / kBN;
+        }
     }
+    const int s_lo = min(nstage, (t_lo + kBwdSub - 1) / kBwdSub);
+    const int s_hi = max(s_lo, min(nstage, t_hi / kBwdSub));
+    for (int st = 0; st < s_lo; ++st) stage_body(st, std::false_type{});
+    for (int st = s_lo; st < s_hi; ++st) stage_body(st, std::true_type{});
+    for (int st = s_hi; st < nstage; ++st) stage_body(st, std::false_type{});
 
     if (xv) {
         T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.H + hh) * n_x + x) * DS;
@@ -741,7 +778,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 // most queries; for rectangular shapes the kind with the longer stream goes
 // first), walked in the order of block_order.
 template <typename T, int DT, int DS, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void streamkl_bwd_kernel(BwdParams pq, BwdParams pk) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void streamkl_bwd_kernel(BwdParams pq,
+                                                                                            BwdParams pk) {
     constexpr int STAGE = kBwdSub * (Tile<T, DT>::kBytes + Tile<T, DS>::kBytes);
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
     // per-query -LSE_t log2 e, -LSE_s log2 e, g tau_s of each stage's rows (dk_s blocks)

@@ -40,17 +40,24 @@ def _kernels(lines):
 
 
 def test_every_kernel_barrier_drains_vmcnt_first(asm):
+    """Walking back from each s_barrier, the nearest s_waitcnt drains vmcnt and
+    no vector-memory load is issued between it and the barrier."""
     kernels = list(_kernels(asm))
     assert len(kernels) == 32  # {bf16, f32} x {64, 128}^2 x {causal, not} for each of fwd and bwd
     for name, body in kernels:
         nbar = 0
         for k, line in enumerate(body):
-            if line.strip().startswith("s_barrier"):
-                nbar += 1
-                j = k - 1
-                while body[j].strip().startswith(";") or not body[j].strip() or body[j].startswith("."):
-                    j -= 1
-                assert "s_waitcnt" in body[j] and "vmcnt(0)" in body[j], f"{name}: barrier at +{k} after {body[j]!r}"
+            if not line.strip().startswith("s_barrier"):
+                continue
+            nbar += 1
+            j = k - 1
+            while j > 0 and not body[j].strip().startswith("s_waitcnt"):
+                op = body[j].strip().split(" ")[0]
+                assert not op.startswith(("global_load", "buffer_load", "flat_load")), \
+                    f"{name}: load {body[j]!r} between the last wait and the barrier at +{k}"
+                assert not re.match(r"^\.LBB|^; %bb", body[j]), f"{name}: barrier at +{k} starts a block without a wait"
+                j -= 1
+            assert "vmcnt(0)" in body[j], f"{name}: barrier at +{k} after {body[j]!r}"
         assert nbar >= 2, name
 
 
