@@ -549,28 +549,50 @@ __device__ inline void tile_ds(const f32x16 &xt, const f32x16 &xs, float ct, flo
 // accumulator layout (its row order is the contraction order); the matching
 // transposed student rows come from the row-major LDS tile via
 // ds_read_b64_tr_b16 (fp32 inputs: one ds_read_b32 per k-step).
+// Transposed student operands of one tile's gradient MFMAs (bf16): fragment
+// [ks][t] holds Y_s^T rows t*32 + (lane % 32), contraction rows 16 ks + 8 (lane / 32)
+// .. +8 of the tile, read from the row-major LDS tile with ds_read_b64_tr_b16.
+template <int DS>
+struct TrFrags {
+    bf16x8 a[2][DS / kTile];
+};
+template <int DS>
+__device__ inline void tr_load(TrFrags<DS> &f, const char *ys, int lane, int hf, int ks_lo, int ks_hi) {
+    using L = Tile<bf16_t, DS>;
+    const int trow = 4 * hf + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int ks = ks_lo; ks < ks_hi; ++ks) {
+#pragma unroll
+        for (int t = 0; t < DS / kTile; ++t) {
+            const int r0 = 16 * ks + trow, col = t * kTile + tcol;
+            const char *a0 = ys + L::chunk_off(r0, col >> 3) + (col & 7) * 2;
+            const char *a1 = ys + L::chunk_off(r0 + 8, col >> 3) + (col & 7) * 2;
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(a0));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(a1));
+            const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0), b1 = __builtin_bit_cast(bf16x4, v1);
+            f.a[ks][t] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        }
+    }
+}
+
+// G^T[d][x] += Y_s^T[d][y] . dS[y][x].  dS is the B operand straight from the
+// accumulator layout (its row order is the contraction order); the matching
+// transposed student rows come from the row-major LDS tile via
+// ds_read_b64_tr_b16, loaded beforehand by tr_load (fp32 inputs: one
+// ds_read_b32 per k-step, here).
 template <typename T, int DS>
-__device__ inline void tile_grad(f32x16 *G, const float *dsv, const char *ys, int lane, int hf, int l32) {
+__device__ inline void tile_grad(f32x16 *G, const float *dsv, const void *trf, const char *ys, int hf, int l32) {
     using L = Tile<T, DS>;
     if constexpr (sizeof(T) == 2) {
-        const int trow = 4 * hf + ((lane & 15) >> 2);
-        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const TrFrags<DS> &f = *static_cast<const TrFrags<DS> *>(trf);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 bfrag;
 #pragma unroll
             for (int e = 0; e < 8; ++e) bfrag[e] = (bf16_t)dsv[ks * 8 + e];
 #pragma unroll
-            for (int t = 0; t < DS / kTile; ++t) {
-                const int r0 = 16 * ks + trow, col = t * kTile + tcol;
-                const char *a0 = ys + L::chunk_off(r0, col >> 3) + (col & 7) * 2;
-                const char *a1 = ys + L::chunk_off(r0 + 8, col >> 3) + (col & 7) * 2;
-                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(a0));
-                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(a1));
-                const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0), b1 = __builtin_bit_cast(bf16x4, v1);
-                const bf16x8 afrag = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                G[t] = Ty<bf16_t>::mma(afrag, bfrag, G[t]);
-            }
+            for (int t = 0; t < DS / kTile; ++t) G[t] = Ty<bf16_t>::mma(f.a[ks][t], bfrag, G[t]);
         }
     } else {
 #pragma unroll
@@ -585,6 +607,9 @@ __device__ inline void tile_grad(f32x16 *G, const float *dsv, const char *ys, in
     }
 }
 
+#ifndef STREAMKL_TR_EARLY
+#define STREAMKL_TR_EARLY 1  // k-steps of transposed operands read before the dS arithmetic
+#endif
 #ifndef STREAMKL_BWD_SUB
 #define STREAMKL_BWD_SUB 2
 #endif
@@ -691,24 +716,37 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     store_rows(0);
     dma_barrier();
 
-    auto ds_grad = [&](const f32x16 &cur_t, const f32x16 &cur_s, int it, int stage, int sub, bool m_cur) {
+    auto ds_grad = [&](const f32x16 &cur_t, const f32x16 &cur_s, int it, int stage, int sub, bool m_cur,
+                       auto early_tag) {
+        constexpr int EARLY = decltype(early_tag)::value;  // k-steps of transposed reads before dS
         const int y0 = ystart + it * kBN;
         const float *rv = &rowv[DKMODE ? stage : 0][0][DKMODE ? sub * kBN : 0];
+        const char *ys = smem + stage * STAGE + sub * PAIR + TileT::kBytes;
+        // the transposed operand reads go out before the dS arithmetic hides them
+        TrFrags<(sizeof(T) == 2 ? DS : kTile)> trf;
+        if constexpr (sizeof(T) == 2) {
+            if (EARLY > 0) {
+                tr_load<DS>(trf, ys, lane, hf, 0, EARLY);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         float dsv[16];
         if (m_cur)
             tile_ds<true, CAUSAL, DKMODE, kBwdRows>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
         else
             tile_ds<false, CAUSAL, DKMODE, kBwdRows>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
-        tile_grad<T, DS>(G, dsv, smem + stage * STAGE + sub * PAIR + TileT::kBytes, lane, hf, l32);
+        if constexpr (sizeof(T) == 2) {
+            if (EARLY < 2) tr_load<DS>(trf, ys, lane, hf, EARLY, 2);
+        }
+        tile_grad<T, DS>(G, dsv, &trf, ys, hf, l32);
     };
 
     // One ring stage: loads for the next stage, the tiles of this one, barrier.
     // PLAIN stages hold only tiles that are active and unmasked for this wave,
     // so their body has no branches (branches around the MFMA chain make the
     // compiler copy the gradient accumulators at every join).
-    auto stage_body = [&](int st, auto plain_tag) {
+    auto stage_body = [&](int st, auto plain_tag, int sc) {  // sc = st % 2, the ring slot
         constexpr bool PLAIN = decltype(plain_tag)::value;
-        const int sc = st & 1;
         if (st + 1 < nstage) {
             issue(st + 1, sc ^ 1);
             load_rows(st + 1);
@@ -720,11 +758,11 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
             if (PLAIN) {
                 const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
                 const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
-                ds_grad(cur_t, cur_s, it, sc, sub, false);
+                ds_grad(cur_t, cur_s, it, sc, sub, false, std::integral_constant<int, STREAMKL_TR_EARLY>{});
             } else if (it < ntile && active(it)) {
                 const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
                 const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
-                ds_grad(cur_t, cur_s, it, sc, sub, need_mask(it));
+                ds_grad(cur_t, cur_s, it, sc, sub, need_mask(it), std::integral_constant<int, 0>{});
             }
         }
         if (st + 1 < nstage) store_rows(sc ^ 1);
@@ -748,9 +786,19 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     }
     const int s_lo = min(nstage, (t_lo + kBwdSub - 1) / kBwdSub);
     const int s_hi = max(s_lo, min(nstage, t_hi / kBwdSub));
-    for (int st = 0; st < s_lo; ++st) stage_body(st, std::false_type{});
-    for (int st = s_lo; st < s_hi; ++st) stage_body(st, std::true_type{});
-    for (int st = s_hi; st < nstage; ++st) stage_body(st, std::false_type{});
+    for (int st = 0; st < s_lo; ++st) stage_body(st, std::false_type{}, st & 1);
+    {
+        // plain stages two at a time, so that the ring slot, and with it every
+        // LDS address, is a compile-time offset
+        int st = s_lo;
+        if (st < s_hi && (st & 1)) stage_body(st++, std::true_type{}, 1);
+        for (; st + 1 < s_hi; st += 2) {
+            stage_body(st, std::true_type{}, 0);
+            stage_body(st + 1, std::true_type{}, 1);
+        }
+        if (st < s_hi) stage_body(st, std::true_type{}, 0);
+    }
+    for (int st = s_hi; st < nstage; ++st) stage_body(st, std::false_type{}, st & 1);
 
     if (xv) {
         T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.H + hh) * n_x + x) * DS;
