@@ -512,17 +512,22 @@ __device__ inline int bwd_tiles(const BwdParams &p, int xb) {
 // P = 2^(x * c - LSE * log2 e).  Per-query values (-LSE_t log2 e, -LSE_s log2 e,
 // g tau_s) are per lane when the queries are the stationary items, else they
 // come from the stage's LDS row-value block rv[3][kBN].
-template <bool MASK, bool CAUSAL, bool DKMODE, int RS = kBN>
+//
+// FOLD: the upstream weight w = g tau_s is already inside the exponents as
+// log2 |w| (both per-query values carry it), so dS / sign(w) = P'_s - P'_t and
+// the sign is applied to the finished gradient; otherwise the third per-query
+// value is w and multiplies the difference.
+template <bool MASK, bool CAUSAL, bool DKMODE, int RS = kBN, bool FOLD = false>
 __device__ inline void tile_ds(const f32x16 &xt, const f32x16 &xs, float ct, float cs, float nlt, float nls,
                                float gts, const float *rv, int y0, int hf, int x, int n_y, int off, float *dsv) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-        f32x4 a_t, a_s, gg;
+        f32x4 a_t, a_s, gg = f32x4{1.f, 1.f, 1.f, 1.f};
         if (DKMODE) {
             const int r0 = grp * 8 + hf * 4;
             a_t = *reinterpret_cast<const f32x4 *>(rv + r0);
             a_s = *reinterpret_cast<const f32x4 *>(rv + RS + r0);
-            gg = *reinterpret_cast<const f32x4 *>(rv + 2 * RS + r0);
+            if (!FOLD) gg = *reinterpret_cast<const f32x4 *>(rv + 2 * RS + r0);
         } else {
             a_t = f32x4{nlt, nlt, nlt, nlt};
             a_s = f32x4{nls, nls, nls, nls};
@@ -533,7 +538,7 @@ __device__ inline void tile_ds(const f32x16 &xt, const f32x16 &xs, float ct, flo
             const int i = grp * 4 + e;
             const float pt = fast_exp2(fmaf(xt[i], ct, a_t[e]));
             const float ps = fast_exp2(fmaf(xs[i], cs, a_s[e]));
-            float d = gg[e] * (ps - pt);
+            float d = FOLD ? ps - pt : gg[e] * (ps - pt);
             if (MASK) {
                 const int y = y0 + acc_row(i, hf);
                 bool ok = y < n_y;
@@ -621,14 +626,18 @@ constexpr int kBwdRows = kBwdSub * kBN;
 // One (stationary block, head) of the backward: the kBlockX stationary items
 // x0 .. x0 + kBlockX - 1 (queries for dq_s, keys for dk_s) of head bh, with the
 // other kind streamed through a two-stage LDS ring.  Two waves per SIMD overlap
-// each other's MFMA and VALU phases.
-template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE>
+// each other's MFMA and VALU phases.  GS: the upstream gradient is one scalar.
+template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE, bool GS>
 __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams &p, int xb, int bh, char *smem,
                                                                 float (*rowv)[3][kBwdRows]) {
     using TileT = Tile<T, DT>;
     using TileS = Tile<T, DS>;
     constexpr int PAIR = TileT::kBytes + TileS::kBytes;  // one 32-row tile of both tensors
     constexpr int STAGE = kBwdSub * PAIR;
+    // fold w = g tau_s into the exponents whenever its sign is uniform over each
+    // gradient row's contraction: always for query-major blocks (w belongs to
+    // the stationary query), for key-major blocks when g is a scalar
+    constexpr bool FOLD = !DKMODE || GS;
 
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -674,6 +683,9 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
             }
         }
     };
+    // log2 |w| and sign(w) of the scalar upstream weight (folded key-major case)
+    const float w_all = p.g_scalar * p.tau_s;
+    const float lw_all = log2f(fabsf(w_all));
     float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query y0 + tid (tid < kBwdRows)
     auto load_rows = [&](int st) {
         if (DKMODE && tid < kBwdRows) {
@@ -682,7 +694,12 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
             if (y < n_q) {
                 rv0 = -p.lse_t[rowbase + y] * kLog2e;
                 rv1 = -p.lse_s[rowbase + y] * kLog2e;
-                rv2 = (p.g ? p.g[rowbase + y] : p.g_scalar) * p.tau_s;
+                if (FOLD) {
+                    rv0 += lw_all;
+                    rv1 += lw_all;
+                } else {
+                    rv2 = p.g[rowbase + y] * p.tau_s;
+                }
             }
         }
     };
@@ -690,7 +707,7 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         if (DKMODE && tid < kBwdRows) {
             rowv[stage][0][tid] = rv0;
             rowv[stage][1][tid] = rv1;
-            rowv[stage][2][tid] = rv2;
+            if (!FOLD) rowv[stage][2][tid] = rv2;
         }
     };
 
@@ -703,10 +720,13 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 
     const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
     float nlt = 0.f, nls = 0.f, gts = 0.f;  // per-lane row values (dq mode)
+    float gsign = w_all < 0.f ? -1.f : 1.f;  // sign(w) applied to the finished gradient when folded
     if (!DKMODE && xv) {
-        nlt = -p.lse_t[rowbase + x] * kLog2e;
-        nls = -p.lse_s[rowbase + x] * kLog2e;
-        gts = (p.g ? p.g[rowbase + x] : p.g_scalar) * p.tau_s;
+        const float wq = (GS ? p.g_scalar : p.g[rowbase + x]) * p.tau_s;
+        const float lw = log2f(fabsf(wq));
+        nlt = -p.lse_t[rowbase + x] * kLog2e + lw;
+        nls = -p.lse_s[rowbase + x] * kLog2e + lw;
+        gsign = wq < 0.f ? -1.f : 1.f;
     }
 
     f32x16 G[DS / kTile];
@@ -732,9 +752,9 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         }
         float dsv[16];
         if (m_cur)
-            tile_ds<true, CAUSAL, DKMODE, kBwdRows>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
+            tile_ds<true, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
         else
-            tile_ds<false, CAUSAL, DKMODE, kBwdRows>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
+            tile_ds<false, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
         if constexpr (sizeof(T) == 2) {
             if (EARLY < 2) tr_load<DS>(trf, ys, lane, hf, EARLY, 2);
         }
@@ -800,6 +820,10 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     }
     for (int st = s_hi; st < nstage; ++st) stage_body(st, std::false_type{}, st & 1);
 
+    if (FOLD) {
+#pragma unroll
+        for (int t = 0; t < DS / kTile; ++t) G[t] *= gsign;
+    }
     if (xv) {
         T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.H + hh) * n_x + x) * DS;
 #pragma unroll
@@ -825,7 +849,7 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 // mask high query blocks see the most keys and low key blocks are seen by the
 // most queries; for rectangular shapes the kind with the longer stream goes
 // first), walked in the order of block_order.
-template <typename T, int DT, int DS, bool CAUSAL>
+template <typename T, int DT, int DS, bool CAUSAL, bool GS>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void streamkl_bwd_kernel(BwdParams pq,
                                                                                             BwdParams pk) {
     constexpr int STAGE = kBwdSub * (Tile<T, DT>::kBytes + Tile<T, DS>::kBytes);
@@ -854,8 +878,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     }
     const bool dk = !(r - lo >= nk || (lo < nq && a_first(lo, r - lo)));
     const int idx = dk ? r - lo : nq - 1 - lo;
-    if (dk) bwd_block<T, DT, DS, CAUSAL, true>(pk, idx, bh, smem, rowv);
-    else bwd_block<T, DT, DS, CAUSAL, false>(pq, idx, bh, smem, rowv);
+    if (dk) bwd_block<T, DT, DS, CAUSAL, true, GS>(pk, idx, bh, smem, rowv);
+    else bwd_block<T, DT, DS, CAUSAL, false, GS>(pq, idx, bh, smem, rowv);
 }
 
 // ================================================================= host side
@@ -934,9 +958,9 @@ template <typename T, int DT, int DS, bool C>
 void launch_fwd(const FwdParams &p, int grid, hipStream_t s) {
     hipLaunchKernelGGL((streamkl_fwd_kernel<T, DT, DS, C>), dim3(grid), dim3(kThreads), 0, s, p);
 }
-template <typename T, int DT, int DS, bool C>
+template <typename T, int DT, int DS, bool C, bool GS>
 void launch_bwd(const BwdParams &pq, const BwdParams &pk, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C>), dim3(grid), dim3(kThreads), 0, s, pq, pk);
+    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C, GS>), dim3(grid), dim3(kThreads), 0, s, pq, pk);
 }
 
 template <typename T, int DT, int DS>
@@ -944,8 +968,9 @@ fwd_launch_t pick_fwd2(int causal) {
     return causal ? launch_fwd<T, DT, DS, true> : launch_fwd<T, DT, DS, false>;
 }
 template <typename T, int DT, int DS>
-bwd_launch_t pick_bwd2(int causal) {
-    return causal ? launch_bwd<T, DT, DS, true> : launch_bwd<T, DT, DS, false>;
+bwd_launch_t pick_bwd2(int causal, bool gs) {
+    if (gs) return causal ? launch_bwd<T, DT, DS, true, true> : launch_bwd<T, DT, DS, false, true>;
+    return causal ? launch_bwd<T, DT, DS, true, false> : launch_bwd<T, DT, DS, false, false>;
 }
 template <typename T>
 fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
@@ -956,11 +981,11 @@ fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
     return nullptr;
 }
 template <typename T>
-bwd_launch_t pick_bwd1(int d_t, int d_s, int causal) {
-    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal);
-    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal);
-    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal);
-    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal);
+bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool gs) {
+    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal, gs);
+    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal, gs);
+    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal, gs);
+    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal, gs);
     return nullptr;
 }
 
@@ -1077,7 +1102,8 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
             }
         pp[0].rank_major = pp[1].rank_major = want_rank_major(mn, mx, tot, (int64_t)B * H);
     }
-    bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal) : pick_bwd1<float>(d_t, d_s, causal);
+    const bool gs = grad_rows == nullptr;
+    bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal, gs) : pick_bwd1<float>(d_t, d_s, causal, gs);
     if (!fn) return STREAMKL_ERR_UNSUPPORTED;
     fn(pp[0], pp[1], B * H * (pp[0].n_xblk + pp[1].n_xblk), hs);
     if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;

@@ -85,6 +85,27 @@ def test_random_upstream_gradient(name, w):
     _full_compare(w, inputs.make(w), g=g)
 
 
+@pytest.mark.parametrize("gs", [-2.5, 0.0, 3.0])
+@pytest.mark.parametrize("name,w", [SMALL[1], SMALL[4]], ids=["f32_128x64_tail", "bf16_corr_causal_300"])
+def test_scalar_upstream_gradient(name, w, gs):
+    """A scalar upstream gradient is folded into the exponents as log2|g tau_s|
+    with its sign applied to the finished gradient: check negative, zero and
+    positive values against the oracle."""
+    x = inputs.make(w)
+    d = to_device(x, w.dtype)
+    kl, lt, ls, _ = skl.streamkl_fwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], w.tau_t, w.tau_s, w.causal)
+    dq, dk = skl.streamkl_bwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], lt, ls, grad_scalar=gs,
+                              tau_t=w.tau_t, tau_s=w.tau_s, causal=w.causal)
+    torch.cuda.synchronize()
+    xo = as_f64(x)
+    rdq, rdk = oracle.bwd(xo["q_t"], xo["k_t"], xo["q_s"], xo["k_s"], w.tau_t, w.tau_s, w.causal, g=gs)
+    if gs == 0.0:
+        assert not torch.any(dq) and not torch.any(dk)
+        return
+    check_grad(dq.float().cpu().numpy(), rdq, w.dtype, "dq_s")
+    check_grad(dk.float().cpu().numpy(), rdk, w.dtype, "dk_s")
+
+
 EDGE = [
     ("one_by_one", W["mixed_dims_2k"].resized(B=1, H=1, n_q=1, n_k=1, d_t=64, d_s=64, seed=201)),
     ("one_by_one_causal", W["mixed_dims_2k"].resized(B=1, H=1, n_q=1, n_k=1, d_t=64, d_s=64, causal=True, seed=202)),
@@ -179,9 +200,15 @@ def test_autograd_function_and_extra_memory():
     # plus the gradients; allow allocator rounding
     assert peak <= grads + 4 * 4 * rows + (1 << 20), (peak, grads, rows)
     ref = skl.streamkl_fwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"])
-    rg = skl.streamkl_bwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], ref[1], ref[2])
+    ones = torch.ones_like(ref[0])
+    rg = skl.streamkl_bwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], ref[1], ref[2], grad_rows=ones)
     assert torch.equal(kl.detach(), ref[0])
     assert torch.equal(qs.grad, rg[0]) and torch.equal(ks.grad, rg[1])
+    # the scalar-gradient path (g folded into the exponents) agrees to rounding
+    sg = skl.streamkl_bwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], ref[1], ref[2], grad_scalar=1.0)
+    torch.cuda.synchronize()
+    for a, b in zip(sg, rg):
+        assert rel_l2(a.float().cpu().numpy(), b.float().cpu().numpy()) <= 2e-3
 
 
 # ------------------------------------------------------------------ full sizes
