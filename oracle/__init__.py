@@ -46,6 +46,12 @@ def _load():
     lib.oracle_dq_rows.restype = None
     lib.oracle_dk_keys.argtypes = common + [ctypes.c_void_p, _D, _I, _I, _I, _i64p, _f64p]
     lib.oracle_dk_keys.restype = None
+    lib.oracle_bwd_teacher.argtypes = common + [ctypes.c_void_p, _D, _f64p, _f64p]
+    lib.oracle_bwd_teacher.restype = None
+    lib.oracle_dqt_rows.argtypes = common + [ctypes.c_void_p, _D, _I, _i64p, _f64p]
+    lib.oracle_dqt_rows.restype = None
+    lib.oracle_dkt_keys.argtypes = common + [ctypes.c_void_p, _D, _I, _I, _I, _i64p, _f64p]
+    lib.oracle_dkt_keys.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = _I
     _lib = lib
@@ -139,3 +145,43 @@ def dk_keys(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, b, h, keys, g=None):
 def num_threads():
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def bwd_teacher(q_t, k_t, q_s, k_s, tau_t, tau_s, causal=False, g=None):
+    """dQ_t, dK_t (fp64) of L = sum_r g_r KL_r: gradients with respect to the
+    first (teacher) distribution's queries and keys.  With the two
+    distributions swapped these are the student gradients of the reverse KL."""
+    lib = _load()
+    arrs, (B, H, n_q, n_k, d_t, d_s) = _prep(q_t, k_t, q_s, k_s)
+    garr, gs = _g_arg(g, B, H, n_q)
+    dq = np.empty((B, H, n_q, d_t)); dk = np.empty((B, H, n_k, d_t))
+    gp = garr.ctypes.data if garr is not None else None
+    lib.oracle_bwd_teacher(*arrs, B, H, n_q, n_k, d_t, d_s, float(tau_t), float(tau_s), int(causal),
+                           gp, gs, dq, dk)
+    return dq, dk
+
+
+def dqt_rows(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, rows, g=None):
+    """dQ_t rows [len(rows), d_t] for flat row indices."""
+    lib = _load()
+    arrs, (B, H, n_q, n_k, d_t, d_s) = _prep(q_t, k_t, q_s, k_s)
+    garr, gs = _g_arg(g, B, H, n_q)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, d_t))
+    gp = garr.ctypes.data if garr is not None else None
+    lib.oracle_dqt_rows(*arrs, B, H, n_q, n_k, d_t, d_s, float(tau_t), float(tau_s), int(causal),
+                        gp, gs, rows.size, rows, out)
+    return out
+
+
+def dkt_keys(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, b, h, keys, g=None):
+    """dK_t rows [len(keys), d_t] for keys of head (b, h)."""
+    lib = _load()
+    arrs, (B, H, n_q, n_k, d_t, d_s) = _prep(q_t, k_t, q_s, k_s)
+    garr, gs = _g_arg(g, B, H, n_q)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    out = np.empty((keys.size, d_t))
+    gp = garr.ctypes.data if garr is not None else None
+    lib.oracle_dkt_keys(*arrs, B, H, n_q, n_k, d_t, d_s, float(tau_t), float(tau_s), int(causal),
+                        gp, gs, int(b), int(h), keys.size, keys, out)
+    return out

@@ -25,7 +25,9 @@
  *    j <= i + (n_k - n_q); causal with n_q > n_k is rejected by the caller;
  *  - the reduced scalar is the plain sum over all B*H*N_Q rows;
  *  - gradients are for L = sum_r g_r * KL_r with respect to the student
- *    queries and keys (the teacher is a fixed target).
+ *    queries and keys (the teacher is a fixed target); the *_teacher and
+ *    *_dqt / *_dkt functions give the same loss's gradients with respect to the
+ *    teacher (first-argument) queries and keys.
  *
  * Layout: every tensor is contiguous [B][H][N][d] of fp64 values (bf16 and
  * fp32 inputs are passed already widened, which is exact); outputs are fp64.
@@ -349,6 +351,188 @@ void oracle_dk_keys(const double *q_t, const double *k_t, const double *q_s, con
         }
 #pragma omp critical
         for (size_t x = 0; x < (size_t)n_keys * d_s; ++x)
+            dk[x] += part[x];
+        free(st);
+        free(ss);
+        free(dS);
+        free(part);
+    }
+}
+
+/*
+ * Gradients with respect to the FIRST (teacher) distribution.
+ *
+ * dS_t row for query i of one head:
+ *   dS_t[j] = g * tau_t * P_t[j] * (log P_t[j] - log P_s[j] - KL_i)
+ * for allowed j, 0 otherwise.  This is the derivative of g * KL_i with respect
+ * to the teacher score s_t[j] = tau_t * q_t . k_t[j].  Writing
+ * L[k] = log P_t[k] - log P_s[k] and dP_t[k]/ds_t[j] = P_t[k] (delta_kj - P_t[j]):
+ *   d/ds_t[j] sum_k P_t[k] L[k]
+ *     = sum_k P_t[k] (delta_kj - P_t[j]) L[k] + sum_k P_t[k] dL[k]/ds_t[j]
+ *     = P_t[j] (L[j] - KL_i) + sum_k P_t[k] (delta_kj - P_t[j])
+ *     = P_t[j] (L[j] - KL_i) + 0.
+ * Swapping the two distributions (student first) gives the student gradient of
+ * the reverse divergence KL(P_s || P_t) with the same formula.
+ */
+static void row_dS_teacher(const double *qt, const double *kt, const double *qs, const double *ks,
+                           int dt, int ds, int n, int n_k, double tau_t, double tau_s, double g,
+                           double *st, double *ss, double *dS)
+{
+    score_row(qt, kt, dt, n, tau_t, st);
+    score_row(qs, ks, ds, n, tau_s, ss);
+    double lt = log_sum_exp(st, n);
+    double ls = log_sum_exp(ss, n);
+    double kl = 0.0;
+    for (int j = 0; j < n; ++j) {
+        double logpt = st[j] - lt;
+        double logps = ss[j] - ls;
+        double pt = exp(logpt);
+        if (pt != 0.0)
+            kl += pt * (logpt - logps);
+    }
+    for (int j = 0; j < n; ++j) {
+        double logpt = st[j] - lt;
+        double logps = ss[j] - ls;
+        double pt = exp(logpt);
+        dS[j] = pt != 0.0 ? g * tau_t * pt * (logpt - logps - kl) : 0.0;
+    }
+    for (int j = n; j < n_k; ++j)
+        dS[j] = 0.0;
+}
+
+/*
+ * Teacher backward over every row: dq_t [B][H][n_q][d_t] and dk_t [B][H][n_k][d_t]
+ * (fp64, overwritten) for L = sum_r g_r KL_r:
+ *   dq_t[i] = sum_j dS_t[i][j] k_t[j],   dk_t[j] = sum_i dS_t[i][j] q_t[i].
+ */
+void oracle_bwd_teacher(const double *q_t, const double *k_t, const double *q_s, const double *k_s,
+                        int B, int H, int n_q, int n_k, int d_t, int d_s,
+                        double tau_t, double tau_s, int causal,
+                        const double *g_rows, double g_scalar,
+                        double *dq_t, double *dk_t)
+{
+    const int R = ORACLE_ROWBLOCK;
+    double *dS = (double *)malloc(sizeof(double) * (size_t)R * (size_t)(n_k > 0 ? n_k : 1));
+    memset(dk_t, 0, sizeof(double) * (size_t)B * H * n_k * d_t);
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const double *kt = k_t + head_off(b, h, H, n_k, d_t);
+            const double *ks = k_s + head_off(b, h, H, n_k, d_s);
+            double *dkh = dk_t + head_off(b, h, H, n_k, d_t);
+            for (int i0 = 0; i0 < n_q; i0 += R) {
+                int nr = (n_q - i0 < R) ? (n_q - i0) : R;
+#pragma omp parallel
+                {
+                    double *st = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+                    double *ss = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+#pragma omp for schedule(static, 1)
+                    for (int t = 0; t < nr; ++t) {
+                        int i = i0 + t;
+                        long long r = ((long long)b * H + h) * n_q + i;
+                        double g = g_rows ? g_rows[r] : g_scalar;
+                        int n = allowed_keys(i, n_q, n_k, causal);
+                        const double *qt = q_t + head_off(b, h, H, n_q, d_t) + (size_t)i * d_t;
+                        const double *qs = q_s + head_off(b, h, H, n_q, d_s) + (size_t)i * d_s;
+                        double *dSi = dS + (size_t)t * n_k;
+                        row_dS_teacher(qt, kt, qs, ks, d_t, d_s, n, n_k, tau_t, tau_s, g, st, ss, dSi);
+                        double *dqi = dq_t + head_off(b, h, H, n_q, d_t) + (size_t)i * d_t;
+                        for (int c = 0; c < d_t; ++c) {
+                            double acc = 0.0;
+                            for (int j = 0; j < n_k; ++j)
+                                acc += dSi[j] * kt[(size_t)j * d_t + c];
+                            dqi[c] = acc;
+                        }
+                    }
+                    free(st);
+                    free(ss);
+#pragma omp for schedule(static)
+                    for (int j = 0; j < n_k; ++j)
+                        for (int t = 0; t < nr; ++t) {
+                            double w = dS[(size_t)t * n_k + j];
+                            if (w == 0.0) continue;
+                            const double *qt = q_t + head_off(b, h, H, n_q, d_t) + (size_t)(i0 + t) * d_t;
+                            for (int c = 0; c < d_t; ++c)
+                                dkh[(size_t)j * d_t + c] += w * qt[c];
+                        }
+                }
+            }
+        }
+    free(dS);
+}
+
+/* dq_t for a chosen set of rows only (flat row index as in oracle_fwd_rows); dq: [n_rows][d_t]. */
+void oracle_dqt_rows(const double *q_t, const double *k_t, const double *q_s, const double *k_s,
+                     int B, int H, int n_q, int n_k, int d_t, int d_s,
+                     double tau_t, double tau_s, int causal,
+                     const double *g_rows, double g_scalar,
+                     int n_rows, const int64_t *rows, double *dq)
+{
+    (void)B;
+#pragma omp parallel
+    {
+        double *st = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+        double *ss = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+        double *dS = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n_rows; ++t) {
+            long long r = rows[t];
+            int i = (int)(r % n_q);
+            long long bh = r / n_q;
+            int h = (int)(bh % H), b = (int)(bh / H);
+            double g = g_rows ? g_rows[r] : g_scalar;
+            int n = allowed_keys(i, n_q, n_k, causal);
+            const double *qt = q_t + head_off(b, h, H, n_q, d_t) + (size_t)i * d_t;
+            const double *qs = q_s + head_off(b, h, H, n_q, d_s) + (size_t)i * d_s;
+            const double *kt = k_t + head_off(b, h, H, n_k, d_t);
+            const double *ks = k_s + head_off(b, h, H, n_k, d_s);
+            row_dS_teacher(qt, kt, qs, ks, d_t, d_s, n, n_k, tau_t, tau_s, g, st, ss, dS);
+            for (int c = 0; c < d_t; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < n_k; ++j)
+                    acc += dS[j] * kt[(size_t)j * d_t + c];
+                dq[(size_t)t * d_t + c] = acc;
+            }
+        }
+        free(st);
+        free(ss);
+        free(dS);
+    }
+}
+
+/* dk_t for chosen keys of ONE head (b, h): dk[t][c] = sum_i dS_t[i][key_t] q_t[i][c]. */
+void oracle_dkt_keys(const double *q_t, const double *k_t, const double *q_s, const double *k_s,
+                     int B, int H, int n_q, int n_k, int d_t, int d_s,
+                     double tau_t, double tau_s, int causal,
+                     const double *g_rows, double g_scalar,
+                     int b, int h, int n_keys, const int64_t *keys, double *dk)
+{
+    (void)B;
+    const double *kt = k_t + head_off(b, h, H, n_k, d_t);
+    const double *ks = k_s + head_off(b, h, H, n_k, d_s);
+    memset(dk, 0, sizeof(double) * (size_t)n_keys * d_t);
+#pragma omp parallel
+    {
+        double *st = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+        double *ss = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+        double *dS = (double *)malloc(sizeof(double) * (size_t)(n_k > 0 ? n_k : 1));
+        double *part = (double *)calloc((size_t)n_keys * d_t, sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int i = 0; i < n_q; ++i) {
+            long long r = ((long long)b * H + h) * n_q + i;
+            double g = g_rows ? g_rows[r] : g_scalar;
+            int n = allowed_keys(i, n_q, n_k, causal);
+            const double *qt = q_t + head_off(b, h, H, n_q, d_t) + (size_t)i * d_t;
+            const double *qs = q_s + head_off(b, h, H, n_q, d_s) + (size_t)i * d_s;
+            row_dS_teacher(qt, kt, qs, ks, d_t, d_s, n, n_k, tau_t, tau_s, g, st, ss, dS);
+            for (int t = 0; t < n_keys; ++t) {
+                double w = dS[keys[t]];
+                if (w == 0.0) continue;
+                for (int c = 0; c < d_t; ++c)
+                    part[(size_t)t * d_t + c] += w * qt[c];
+            }
+        }
+#pragma omp critical
+        for (size_t x = 0; x < (size_t)n_keys * d_t; ++x)
             dk[x] += part[x];
         free(st);
         free(ss);
