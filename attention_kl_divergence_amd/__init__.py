@@ -49,6 +49,9 @@ def load_library():
     lib.streamkl_fwd.restype = i
     lib.streamkl_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, vp, vp, vp, f, vp, vp, vp]
     lib.streamkl_bwd.restype = i
+    lib.streamkl_bwd_teacher.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, vp, vp, vp, vp, f,
+                                         vp, vp, vp]
+    lib.streamkl_bwd_teacher.restype = i
     lib.streamkl_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.streamkl_bwd_workspace_size.restype = ctypes.c_size_t
     lib.streamkl_status_string.argtypes = [i]
@@ -162,31 +165,63 @@ def streamkl_bwd(q_t, k_t, q_s, k_s, lse_t, lse_s, grad_rows=None, grad_scalar=1
     return dq, dk
 
 
+def streamkl_bwd_teacher(q_t, k_t, q_s, k_s, lse_t, lse_s, kl_rows, grad_rows=None, grad_scalar=1.0,
+                         tau_t=None, tau_s=None, causal=False):
+    """Backward with respect to the first (teacher) distribution: returns
+    (dq_t, dk_t) in the input dtype for L = sum_r g_r KL_r.  kl_rows, lse_t and
+    lse_s are the forward's outputs.  With the two distributions swapped it
+    gives the student gradients of the reverse divergence KL(P_s || P_t)."""
+    import torch
+    lib = load_library()
+    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
+    dev = q_t.device
+    rowargs = (("lse_t", lse_t), ("lse_s", lse_s), ("kl_rows", kl_rows)) + \
+        ((("grad_rows", grad_rows),) if grad_rows is not None else ())
+    for name, t in rowargs:
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, n_q) or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous fp32 [B, H, N_Q] tensor on the inputs' device")
+    dq = torch.empty((B, H, n_q, d_t), dtype=q_t.dtype, device=dev)
+    dk = torch.empty((B, H, n_k, d_t), dtype=q_t.dtype, device=dev)
+    code = lib.streamkl_bwd_teacher(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),
+                                    _dtype_code(q_t), B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s,
+                                    int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr(), kl_rows.data_ptr(),
+                                    grad_rows.data_ptr() if grad_rows is not None else None, float(grad_scalar),
+                                    dq.data_ptr(), dk.data_ptr(), _stream_ptr(dev))
+    _check("streamkl_bwd_teacher", code)
+    return dq, dk
+
+
 def _autograd_function():
     import torch
 
     class StreamKLFunction(torch.autograd.Function):
-        """Per-row attention KL with gradients for the student queries and keys.
+        """Per-row attention KL with gradients for the student queries and keys,
+        and for the teacher queries and keys when those require them.
 
         forward(q_t, k_t, q_s, k_s, tau_t, tau_s, causal) -> kl_rows [B, H, N_Q]
-        The teacher is a fixed target: q_t and k_t get no gradient.
         """
 
         @staticmethod
         def forward(ctx, q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
             kl, lt, ls, _ = streamkl_fwd(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, with_sum=False)
-            ctx.save_for_backward(q_t, k_t, q_s, k_s, lt, ls)
+            ctx.save_for_backward(q_t, k_t, q_s, k_s, lt, ls, kl)
             ctx.cfg = (tau_t, tau_s, causal)
             return kl
 
         @staticmethod
         def backward(ctx, g):
-            q_t, k_t, q_s, k_s, lt, ls = ctx.saved_tensors
+            q_t, k_t, q_s, k_s, lt, ls, kl = ctx.saved_tensors
             tau_t, tau_s, causal = ctx.cfg
             g = g.to(torch.float32).contiguous()
-            dq, dk = streamkl_bwd(q_t, k_t, q_s, k_s, lt, ls, grad_rows=g,
-                                  tau_t=tau_t, tau_s=tau_s, causal=causal)
-            return None, None, dq, dk, None, None, None
+            dq_s = dk_s = dq_t = dk_t = None
+            if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+                dq_s, dk_s = streamkl_bwd(q_t, k_t, q_s, k_s, lt, ls, grad_rows=g,
+                                          tau_t=tau_t, tau_s=tau_s, causal=causal)
+            if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+                dq_t, dk_t = streamkl_bwd_teacher(q_t, k_t, q_s, k_s, lt, ls, kl, grad_rows=g,
+                                                  tau_t=tau_t, tau_s=tau_s, causal=causal)
+            return dq_t, dk_t, dq_s, dk_s, None, None, None
 
     return StreamKLFunction
 
@@ -195,12 +230,14 @@ _fn_cache = None
 
 
 def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
-    """Differentiable per-row attention KL [B, H, N_Q] (gradients flow to q_s and k_s)."""
+    """Differentiable per-row attention KL(P_t || P_s) [B, H, N_Q]; gradients
+    flow to whichever of q_s, k_s, q_t, k_t require them.  The reverse
+    divergence KL(P_s || P_t) is attention_kl(q_s, k_s, q_t, k_t, tau_s, tau_t)."""
     global _fn_cache
     if _fn_cache is None:
         _fn_cache = _autograd_function()
     return _fn_cache.apply(q_t, k_t, q_s, k_s, tau_t, tau_s, causal)
 
 
-__all__ = ["streamkl_fwd", "streamkl_bwd", "attention_kl", "load_library", "supported", "status_string",
+__all__ = ["streamkl_fwd", "streamkl_bwd", "streamkl_bwd_teacher", "attention_kl", "load_library", "supported", "status_string",
            "StreamKLError", "STREAMKL_F32", "STREAMKL_BF16"]

@@ -483,6 +483,7 @@ struct BwdParams {
     bool rank_major;
     float tau_t, tau_s;
     const float *lse_t, *lse_s, *g;
+    const float *kl;  // per-row KL (first-argument gradients only)
     float g_scalar;
     void *out;
 };
@@ -554,6 +555,46 @@ __device__ inline void tile_ds(const f32x16 &xt, const f32x16 &xs, float ct, flo
 // accumulator layout (its row order is the contraction order); the matching
 // transposed student rows come from the row-major LDS tile via
 // ds_read_b64_tr_b16 (fp32 inputs: one ds_read_b32 per k-step).
+// First-argument (teacher) gradient of one 32x32 tile, in fp32:
+//   dS_t[y][x] = w P_t (tau_t x_t - tau_s x_s - b),  b = LSE_t - LSE_s + KL
+// with P_t = 2^(x_t c_t + a), a = -LSE_t log2 e (+ log2 |w| when FOLD, the sign
+// of w then applied to the finished gradient).  Per-query values (a, -b, w)
+// are per lane when the queries are the stationary items, else they come from
+// the stage's LDS row-value block rv[3][RS].
+template <bool MASK, bool CAUSAL, bool DKMODE, int RS, bool FOLD>
+__device__ inline void tile_ds_first(const f32x16 &xt, const f32x16 &xs, float ct, float tau_t, float tau_s,
+                                     float na, float nb, float wq, const float *rv, int y0, int hf, int x, int n_y,
+                                     int off, float *dsv) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+        f32x4 a_t, b_r, ww = f32x4{1.f, 1.f, 1.f, 1.f};
+        if (DKMODE) {
+            const int r0 = grp * 8 + hf * 4;
+            a_t = *reinterpret_cast<const f32x4 *>(rv + r0);
+            b_r = *reinterpret_cast<const f32x4 *>(rv + RS + r0);
+            if (!FOLD) ww = *reinterpret_cast<const f32x4 *>(rv + 2 * RS + r0);
+        } else {
+            a_t = f32x4{na, na, na, na};
+            b_r = f32x4{nb, nb, nb, nb};
+            ww = f32x4{wq, wq, wq, wq};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = grp * 4 + e;
+            const float pt = fast_exp2(fmaf(xt[i], ct, a_t[e]));
+            const float l = fmaf(xs[i], -tau_s, fmaf(xt[i], tau_t, b_r[e]));
+            float d = FOLD ? pt * l : ww[e] * pt * l;
+            if (MASK) {
+                const int y = y0 + acc_row(i, hf);
+                bool ok = y < n_y;
+                if (CAUSAL) ok = ok && (DKMODE ? (x <= y + off) : (y <= x + off));
+                d = ok ? d : 0.f;
+            }
+            dsv[i] = d;
+        }
+    }
+}
+
 // Transposed student operands of one tile's gradient MFMAs (bf16): fragment
 // [ks][t] holds Y_s^T rows t*32 + (lane % 32), contraction rows 16 ks + 8 (lane / 32)
 // .. +8 of the tile, read from the row-major LDS tile with ds_read_b64_tr_b16.
@@ -627,7 +668,9 @@ constexpr int kBwdRows = kBwdSub * kBN;
 // x0 .. x0 + kBlockX - 1 (queries for dq_s, keys for dk_s) of head bh, with the
 // other kind streamed through a two-stage LDS ring.  Two waves per SIMD overlap
 // each other's MFMA and VALU phases.  GS: the upstream gradient is one scalar.
-template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE, bool GS>
+// FIRST: gradients with respect to the first (teacher) distribution, contracted
+// with the teacher tiles (output width d_t) instead of the student ones.
+template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE, bool GS, bool FIRST>
 __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams &p, int xb, int bh, char *smem,
                                                                 float (*rowv)[3][kBwdRows]) {
     using TileT = Tile<T, DT>;
@@ -638,6 +681,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     // gradient row's contraction: always for query-major blocks (w belongs to
     // the stationary query), for key-major blocks when g is a scalar
     constexpr bool FOLD = !DKMODE || GS;
+    constexpr int DG = FIRST ? DT : DS;  // width of the gradient rows
+    constexpr int GOFF = FIRST ? 0 : TileT::kBytes;  // the contracted tile inside a PAIR
 
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -684,7 +729,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         }
     };
     // log2 |w| and sign(w) of the scalar upstream weight (folded key-major case)
-    const float w_all = p.g_scalar * p.tau_s;
+    const float tau_g = FIRST ? p.tau_t : p.tau_s;  // the scale of the differentiated scores
+    const float w_all = p.g_scalar * tau_g;
     const float lw_all = log2f(fabsf(w_all));
     float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query y0 + tid (tid < kBwdRows)
     auto load_rows = [&](int st) {
@@ -693,12 +739,14 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
             rv0 = rv1 = rv2 = 0.f;
             if (y < n_q) {
                 rv0 = -p.lse_t[rowbase + y] * kLog2e;
-                rv1 = -p.lse_s[rowbase + y] * kLog2e;
+                if (FIRST) rv1 = -(p.lse_t[rowbase + y] - p.lse_s[rowbase + y] + p.kl[rowbase + y]);
+                else rv1 = -p.lse_s[rowbase + y] * kLog2e;
                 if (FOLD) {
                     rv0 += lw_all;
-                    rv1 += lw_all;
+                    if (!FIRST) rv1 += lw_all;
                 } else {
-                    rv2 = p.g[rowbase + y] * p.tau_s;
+                    // per-row weight; the teacher kernels also take this path with a scalar g
+                    rv2 = (p.g ? p.g[rowbase + y] : p.g_scalar) * tau_g;
                 }
             }
         }
@@ -722,16 +770,17 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     float nlt = 0.f, nls = 0.f, gts = 0.f;  // per-lane row values (dq mode)
     float gsign = w_all < 0.f ? -1.f : 1.f;  // sign(w) applied to the finished gradient when folded
     if (!DKMODE && xv) {
-        const float wq = (GS ? p.g_scalar : p.g[rowbase + x]) * p.tau_s;
+        const float wq = ((GS || !p.g) ? p.g_scalar : p.g[rowbase + x]) * tau_g;
         const float lw = log2f(fabsf(wq));
         nlt = -p.lse_t[rowbase + x] * kLog2e + lw;
-        nls = -p.lse_s[rowbase + x] * kLog2e + lw;
+        if (FIRST) nls = -(p.lse_t[rowbase + x] - p.lse_s[rowbase + x] + p.kl[rowbase + x]);
+        else nls = -p.lse_s[rowbase + x] * kLog2e + lw;
         gsign = wq < 0.f ? -1.f : 1.f;
     }
 
-    f32x16 G[DS / kTile];
+    f32x16 G[DG / kTile];
 #pragma unroll
-    for (int t = 0; t < DS / kTile; ++t) G[t] = f32x16{};
+    for (int t = 0; t < DG / kTile; ++t) G[t] = f32x16{};
 
     store_rows(0);
     dma_barrier();
@@ -741,24 +790,35 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         constexpr int EARLY = decltype(early_tag)::value;  // k-steps of transposed reads before dS
         const int y0 = ystart + it * kBN;
         const float *rv = &rowv[DKMODE ? stage : 0][0][DKMODE ? sub * kBN : 0];
-        const char *ys = smem + stage * STAGE + sub * PAIR + TileT::kBytes;
+        const char *ys = smem + stage * STAGE + sub * PAIR + GOFF;
         // the transposed operand reads go out before the dS arithmetic hides them
-        TrFrags<(sizeof(T) == 2 ? DS : kTile)> trf;
+        TrFrags<(sizeof(T) == 2 ? DG : kTile)> trf;
         if constexpr (sizeof(T) == 2) {
             if (EARLY > 0) {
-                tr_load<DS>(trf, ys, lane, hf, 0, EARLY);
+                tr_load<DG>(trf, ys, lane, hf, 0, EARLY);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         float dsv[16];
-        if (m_cur)
-            tile_ds<true, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
-        else
-            tile_ds<false, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y, off, dsv);
-        if constexpr (sizeof(T) == 2) {
-            if (EARLY < 2) tr_load<DS>(trf, ys, lane, hf, EARLY, 2);
+        if constexpr (FIRST) {
+            if (m_cur)
+                tile_ds_first<true, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, p.tau_t, p.tau_s, nlt, nls,
+                                                                    gts, rv, y0, hf, x, n_y, off, dsv);
+            else
+                tile_ds_first<false, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, p.tau_t, p.tau_s, nlt, nls,
+                                                                     gts, rv, y0, hf, x, n_y, off, dsv);
+        } else {
+            if (m_cur)
+                tile_ds<true, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x, n_y,
+                                                              off, dsv);
+            else
+                tile_ds<false, CAUSAL, DKMODE, kBwdRows, FOLD>(cur_t, cur_s, ct, cs, nlt, nls, gts, rv, y0, hf, x,
+                                                               n_y, off, dsv);
         }
-        tile_grad<T, DS>(G, dsv, &trf, ys, hf, l32);
+        if constexpr (sizeof(T) == 2) {
+            if (EARLY < 2) tr_load<DG>(trf, ys, lane, hf, EARLY, 2);
+        }
+        tile_grad<T, DG>(G, dsv, &trf, ys, hf, l32);
     };
 
     // One ring stage: loads for the next stage, the tiles of this one, barrier.
@@ -822,12 +882,12 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 
     if (FOLD) {
 #pragma unroll
-        for (int t = 0; t < DS / kTile; ++t) G[t] *= gsign;
+        for (int t = 0; t < DG / kTile; ++t) G[t] *= gsign;
     }
     if (xv) {
-        T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.H + hh) * n_x + x) * DS;
+        T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.H + hh) * n_x + x) * DG;
 #pragma unroll
-        for (int t = 0; t < DS / kTile; ++t) {
+        for (int t = 0; t < DG / kTile; ++t) {
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
                 const int d0 = t * kTile + grp * 8 + hf * 4;
@@ -849,7 +909,7 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 // mask high query blocks see the most keys and low key blocks are seen by the
 // most queries; for rectangular shapes the kind with the longer stream goes
 // first), walked in the order of block_order.
-template <typename T, int DT, int DS, bool CAUSAL, bool GS>
+template <typename T, int DT, int DS, bool CAUSAL, bool GS, bool FIRST>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void streamkl_bwd_kernel(BwdParams pq,
                                                                                             BwdParams pk) {
     constexpr int STAGE = kBwdSub * (Tile<T, DT>::kBytes + Tile<T, DS>::kBytes);
@@ -878,8 +938,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     }
     const bool dk = !(r - lo >= nk || (lo < nq && a_first(lo, r - lo)));
     const int idx = dk ? r - lo : nq - 1 - lo;
-    if (dk) bwd_block<T, DT, DS, CAUSAL, true, GS>(pk, idx, bh, smem, rowv);
-    else bwd_block<T, DT, DS, CAUSAL, false, GS>(pq, idx, bh, smem, rowv);
+    if (dk) bwd_block<T, DT, DS, CAUSAL, true, GS, FIRST>(pk, idx, bh, smem, rowv);
+    else bwd_block<T, DT, DS, CAUSAL, false, GS, FIRST>(pq, idx, bh, smem, rowv);
 }
 
 // ================================================================= host side
@@ -958,9 +1018,9 @@ template <typename T, int DT, int DS, bool C>
 void launch_fwd(const FwdParams &p, int grid, hipStream_t s) {
     hipLaunchKernelGGL((streamkl_fwd_kernel<T, DT, DS, C>), dim3(grid), dim3(kThreads), 0, s, p);
 }
-template <typename T, int DT, int DS, bool C, bool GS>
+template <typename T, int DT, int DS, bool C, bool GS, bool FIRST>
 void launch_bwd(const BwdParams &pq, const BwdParams &pk, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C, GS>), dim3(grid), dim3(kThreads), 0, s, pq, pk);
+    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C, GS, FIRST>), dim3(grid), dim3(kThreads), 0, s, pq, pk);
 }
 
 template <typename T, int DT, int DS>
@@ -968,9 +1028,12 @@ fwd_launch_t pick_fwd2(int causal) {
     return causal ? launch_fwd<T, DT, DS, true> : launch_fwd<T, DT, DS, false>;
 }
 template <typename T, int DT, int DS>
-bwd_launch_t pick_bwd2(int causal, bool gs) {
-    if (gs) return causal ? launch_bwd<T, DT, DS, true, true> : launch_bwd<T, DT, DS, false, true>;
-    return causal ? launch_bwd<T, DT, DS, true, false> : launch_bwd<T, DT, DS, false, false>;
+bwd_launch_t pick_bwd2(int causal, bool gs, bool first) {
+    // first-argument gradients take the per-row-weight form only (no scalar fold
+    // in key-major blocks), which halves their instantiations
+    if (first) return causal ? launch_bwd<T, DT, DS, true, false, true> : launch_bwd<T, DT, DS, false, false, true>;
+    if (gs) return causal ? launch_bwd<T, DT, DS, true, true, false> : launch_bwd<T, DT, DS, false, true, false>;
+    return causal ? launch_bwd<T, DT, DS, true, false, false> : launch_bwd<T, DT, DS, false, false, false>;
 }
 template <typename T>
 fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
@@ -981,12 +1044,73 @@ fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
     return nullptr;
 }
 template <typename T>
-bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool gs) {
-    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal, gs);
-    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal, gs);
-    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal, gs);
-    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal, gs);
+bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool gs, bool first) {
+    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal, gs, first);
+    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal, gs, first);
+    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal, gs, first);
+    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal, gs, first);
     return nullptr;
+}
+
+// Both backward entry points: gradients of sum_r g_r KL_r with respect to the
+// student (first = false, outputs d_s wide) or the teacher (first = true,
+// outputs d_t wide, needs the forward's per-row KL).
+streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                           streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                           const int64_t *strides, float tau_t, float tau_s, int causal, const float *lse_t,
+                           const float *lse_s, const float *kl_rows, const float *grad_rows, float grad_scalar,
+                           void *dq_out, void *dk_out, bool first, void *stream) {
+    const Shape s{B, H, n_q, n_k, d_t, d_s};
+    int64_t st[12];
+    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, st);
+    if (rc != STREAMKL_OK) return rc;
+    if (!lse_t || !lse_s || !dq_out || !dk_out || (first && !kl_rows)) return STREAMKL_ERR_INVALID;
+    if (!isfinite(grad_scalar)) return STREAMKL_ERR_INVALID;
+    if (((uintptr_t)dq_out) % 16 != 0 || ((uintptr_t)dk_out) % 16 != 0) return STREAMKL_ERR_INVALID;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool bf = dtype == STREAMKL_BF16;
+    BwdParams pp[2];
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool dk = pass == 1;
+        BwdParams &p = pp[pass];
+        p = BwdParams{};
+        // stationary operand first, streamed second
+        const int xi = dk ? 1 : 0, yi = dk ? 0 : 1;  // 0 = queries, 1 = keys (index into q_t/k_t stride groups)
+        const void *tq[2] = {q_t, k_t}, *sq[2] = {q_s, k_s};
+        p.x_t = tq[xi]; p.x_s = sq[xi]; p.y_t = tq[yi]; p.y_s = sq[yi];
+        for (int k = 0; k < 3; ++k) {
+            p.st[0 + k] = st[3 * xi + k];        // teacher of the stationary kind
+            p.st[3 + k] = st[3 * (2 + xi) + k];  // student of the stationary kind
+            p.st[6 + k] = st[3 * yi + k];
+            p.st[9 + k] = st[3 * (2 + yi) + k];
+        }
+        p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
+        p.n_x = dk ? n_k : n_q;
+        p.n_y = dk ? n_q : n_k;
+        p.n_xblk = (p.n_x + kBlockX - 1) / kBlockX;
+        p.tau_t = tau_t; p.tau_s = tau_s;
+        p.lse_t = lse_t; p.lse_s = lse_s; p.g = grad_rows; p.g_scalar = grad_scalar;
+        p.kl = kl_rows;
+        p.out = dk ? dk_out : dq_out;
+    }
+    {
+        int64_t mn = INT64_MAX, mx = 0, tot = 0;
+        for (int pass = 0; pass < 2; ++pass)
+            for (int xb = 0; xb < pp[pass].n_xblk; ++xb) {
+                const int64_t t = bwd_block_tiles(s, causal, pass == 1, xb);
+                mn = std::min(mn, t);
+                mx = std::max(mx, t);
+                tot += t;
+            }
+        pp[0].rank_major = pp[1].rank_major = want_rank_major(mn, mx, tot, (int64_t)B * H);
+    }
+    const bool gs = grad_rows == nullptr;
+    bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal, gs, first)
+                         : pick_bwd1<float>(d_t, d_s, causal, gs, first);
+    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+    fn(pp[0], pp[1], B * H * (pp[0].n_xblk + pp[1].n_xblk), hs);
+    if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    return STREAMKL_OK;
 }
 
 }  // namespace
@@ -1059,55 +1183,18 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
                              const int64_t *strides, float tau_t, float tau_s, int causal, const float *lse_t,
                              const float *lse_s, const float *grad_rows, float grad_scalar, void *dq_s,
                              void *dk_s, void *stream) {
-    const Shape s{B, H, n_q, n_k, d_t, d_s};
-    int64_t st[12];
-    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, st);
-    if (rc != STREAMKL_OK) return rc;
-    if (!lse_t || !lse_s || !dq_s || !dk_s) return STREAMKL_ERR_INVALID;
-    if (!isfinite(grad_scalar)) return STREAMKL_ERR_INVALID;
-    if (((uintptr_t)dq_s) % 16 != 0 || ((uintptr_t)dk_s) % 16 != 0) return STREAMKL_ERR_INVALID;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const bool bf = dtype == STREAMKL_BF16;
-    BwdParams pp[2];
-    for (int pass = 0; pass < 2; ++pass) {
-        const bool dk = pass == 1;
-        BwdParams &p = pp[pass];
-        p = BwdParams{};
-        // stationary operand first, streamed second
-        const int xi = dk ? 1 : 0, yi = dk ? 0 : 1;  // 0 = queries, 1 = keys (index into q_t/k_t stride groups)
-        const void *tq[2] = {q_t, k_t}, *sq[2] = {q_s, k_s};
-        p.x_t = tq[xi]; p.x_s = sq[xi]; p.y_t = tq[yi]; p.y_s = sq[yi];
-        for (int k = 0; k < 3; ++k) {
-            p.st[0 + k] = st[3 * xi + k];        // teacher of the stationary kind
-            p.st[3 + k] = st[3 * (2 + xi) + k];  // student of the stationary kind
-            p.st[6 + k] = st[3 * yi + k];
-            p.st[9 + k] = st[3 * (2 + yi) + k];
-        }
-        p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
-        p.n_x = dk ? n_k : n_q;
-        p.n_y = dk ? n_q : n_k;
-        p.n_xblk = (p.n_x + kBlockX - 1) / kBlockX;
-        p.tau_t = tau_t; p.tau_s = tau_s;
-        p.lse_t = lse_t; p.lse_s = lse_s; p.g = grad_rows; p.g_scalar = grad_scalar;
-        p.out = dk ? dk_s : dq_s;
-    }
-    {
-        int64_t mn = INT64_MAX, mx = 0, tot = 0;
-        for (int pass = 0; pass < 2; ++pass)
-            for (int xb = 0; xb < pp[pass].n_xblk; ++xb) {
-                const int64_t t = bwd_block_tiles(s, causal, pass == 1, xb);
-                mn = std::min(mn, t);
-                mx = std::max(mx, t);
-                tot += t;
-            }
-        pp[0].rank_major = pp[1].rank_major = want_rank_major(mn, mx, tot, (int64_t)B * H);
-    }
-    const bool gs = grad_rows == nullptr;
-    bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal, gs) : pick_bwd1<float>(d_t, d_s, causal, gs);
-    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
-    fn(pp[0], pp[1], B * H * (pp[0].n_xblk + pp[1].n_xblk), hs);
-    if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
-    return STREAMKL_OK;
+    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, lse_t,
+                      lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, stream);
+}
+
+streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                     streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                     const int64_t *strides, float tau_t, float tau_s, int causal,
+                                     const float *lse_t, const float *lse_s, const float *kl_rows,
+                                     const float *grad_rows, float grad_scalar, void *dq_t, void *dk_t,
+                                     void *stream) {
+    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, lse_t,
+                      lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, stream);
 }
 
 }  // extern "C"

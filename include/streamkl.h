@@ -115,6 +115,38 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
                              const float *grad_rows, float grad_scalar,
                              void *dq_s, void *dk_s, void *stream);
 
+/*
+ * Backward with respect to the FIRST (teacher) distribution.  Gradients of the
+ * same loss L = sum_r g_r KL_r with respect to the teacher queries and keys,
+ * for callers that train the teacher as well, or that want the reverse
+ * divergence.  From the forward-KL definition ("Lecture 05 - Where It All
+ * Lands", section 3.1), with L_r[j] = log P_t[j] - log P_s[j]:
+ *     dKL_r / ds_t[j] = P_t[j] (L_r[j] - KL_r)
+ *     dS_t[i][j] = g_r * tau_t * P_t[j] * (s_t[j] - s_s[j] - LSE_t + LSE_s - KL_r)
+ *     dq_t[i] = sum_j dS_t[i][j] k_t[j],     dk_t[j] = sum_i dS_t[i][j] q_t[i]
+ * Reverse divergence: called with the two distributions swapped (student
+ * tensors and tau_s in the teacher slots) after streamkl_fwd on the same
+ * swapped arguments, it returns the student gradients of KL(P_s || P_t), the
+ * mode-seeking direction of "Lecture 05", section 3.4.
+ *
+ *   q_t ... causal   exactly as passed to streamkl_fwd
+ *   lse_t, lse_s,    the forward's outputs for the same inputs
+ *   kl_rows
+ *   grad_rows,       as in streamkl_bwd
+ *   grad_scalar
+ *   dq_t, dk_t       out, input dtype, contiguous [B,H,n_q,d_t] and [B,H,n_k,d_t]
+ *
+ * Same launch structure as streamkl_bwd (one deterministic launch, no
+ * workspace, no atomics); errors as in streamkl_bwd, plus INVALID for a NULL
+ * kl_rows.
+ */
+streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                     streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                     const int64_t *strides, float tau_t, float tau_s, int causal,
+                                     const float *lse_t, const float *lse_s, const float *kl_rows,
+                                     const float *grad_rows, float grad_scalar,
+                                     void *dq_t, void *dk_t, void *stream);
+
 /* Bytes of device memory, beyond the caller's inputs and required outputs, that
  * the library needs for a call of this shape: always 0 here (the saved
  * log-normalisers are an output of streamkl_fwd). */

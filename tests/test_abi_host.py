@@ -106,3 +106,26 @@ def test_python_binding_fails_loudly_without_device_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         skl.streamkl_fwd(x, x, x, x)
+
+
+def test_bwd_teacher_rejects_bad_arguments_before_any_hip_call():
+    lib = skl.load_library()
+
+    def call(**kw):
+        a = dict(q_t=A, k_t=A + 0x100000, q_s=A + 0x200000, k_s=A + 0x300000, dtype=skl.STREAMKL_BF16,
+                 B=2, H=3, n_q=100, n_k=77, d_t=128, d_s=64, tau_t=0.088, tau_s=0.125, causal=0,
+                 lt=A + 0x500000, ls=A + 0x600000, kl=A + 0x680000, g=None, gs=1.0,
+                 dq=A + 0x700000, dk=A + 0x800000)
+        a.update(kw)
+        return lib.streamkl_bwd_teacher(a["q_t"], a["k_t"], a["q_s"], a["k_s"], a["dtype"], a["B"], a["H"],
+                                        a["n_q"], a["n_k"], a["d_t"], a["d_s"], None, a["tau_t"], a["tau_s"],
+                                        a["causal"], a["lt"], a["ls"], a["kl"], a["g"], a["gs"], a["dq"], a["dk"],
+                                        None)
+    assert call(kl=None) == INV
+    assert call(lt=None) == INV
+    assert call(dq=None) == INV
+    assert call(dk=A + 8) == INV
+    assert call(gs=float("inf")) == INV
+    assert call(causal=1) == INV
+    assert call(d_t=32) == UNS
+    assert call(tau_t=-0.5) == INV
