@@ -20,6 +20,8 @@ the kernel source still has the hash recorded there (else null).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--no-baseline-mem] [--cpu-heads N]
+       python bench.py --teacher-grads  (adds the first-argument backward,
+                       timed in its own loop after the headline steps)
        python bench.py --copy-calibration MiB   (a plain device copy of known
                        size, run under the same HBM byte counters to scale them)
 """
@@ -147,6 +149,8 @@ def main():
     ap.add_argument("--no-baseline-mem", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    ap.add_argument("--teacher-grads", action="store_true",
+                    help="also time the first-argument (teacher) backward, outside the headline step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this primitive is measured on one GPU only; multi-GPU runs are not supported "
@@ -257,6 +261,30 @@ def main():
                      "traffic": committed_traffic(dom_kernel, w.name),
                      "ms_per_launch": round(float(np.mean(t_f if dominant == "fwd" else t_b)), 4)},
     }
+    if args.teacher_grads:
+        dqt = torch.empty((B, H, w.n_q, w.d_t), dtype=tdt, device=dev)
+        dkt = torch.empty((B, H, w.n_k, w.d_t), dtype=tdt, device=dev)
+
+        def bwd_teacher():
+            rc = lib.streamkl_bwd_teacher(ptr["q_t"], ptr["k_t"], ptr["q_s"], ptr["k_s"], code, B, H, w.n_q, w.n_k,
+                                          w.d_t, w.d_s, None, w.tau_t, w.tau_s, int(w.causal), lt.data_ptr(),
+                                          ls.data_ptr(), kl.data_ptr(), None, 1.0, dqt.data_ptr(), dkt.data_ptr(), sp)
+            if rc:
+                raise RuntimeError(skl.status_string(rc))
+        for _ in range(args.warmup):
+            bwd_teacher()
+        tev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in tev:
+            e[0].record(stream)
+            bwd_teacher()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        t_t = np.array([e[0].elapsed_time(e[1]) for e in tev])
+        Ft = 2.0 * w.pairs * (3 * w.d_t + w.d_s)  # two score recomputes, dQ_t and dK_t
+        res["bwd_teacher_ms"] = round(float(np.mean(t_t)), 4)
+        res["bwd_teacher_tflops"] = round(Ft / (np.mean(t_t) * 1e-3) / 1e12, 2)
+        print(f"[bench] teacher bwd {np.mean(t_t):.3f} ms ({res['bwd_teacher_tflops']:.1f} TF/s)",
+              file=sys.stderr, flush=True)
     if not args.no_baseline_mem:
         bpk = materialized_baseline_peak(w, d, torch)
         res["materialized_baseline_peak_bytes"] = bpk
