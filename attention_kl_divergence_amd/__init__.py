@@ -52,6 +52,18 @@ def load_library():
     lib.streamkl_bwd_teacher.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, vp, vp, vp, vp, f,
                                          vp, vp, vp]
     lib.streamkl_bwd_teacher.restype = i
+    sz = ctypes.c_size_t
+    lib.streamkl_fwd_partial.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, i, i, vp, vp]
+    lib.streamkl_fwd_partial.restype = i
+    lib.streamkl_fwd_merge.argtypes = [vp, i, ctypes.c_int64, f, f, vp, vp, vp, vp, vp]
+    lib.streamkl_fwd_merge.restype = i
+    lib.streamkl_fwd_split_count.argtypes = [i, i, i, i, i]
+    lib.streamkl_fwd_split_count.restype = i
+    lib.streamkl_fwd_split_workspace_size.argtypes = [i, i, i, i]
+    lib.streamkl_fwd_split_workspace_size.restype = sz
+    lib.streamkl_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, i, vp, sz, vp, vp, vp,
+                                       vp, vp]
+    lib.streamkl_fwd_split.restype = i
     lib.streamkl_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.streamkl_bwd_workspace_size.restype = ctypes.c_size_t
     lib.streamkl_status_string.argtypes = [i]
@@ -116,11 +128,13 @@ def _taus(tau_t, tau_s, d_t, d_s):
             float(1.0 / math.sqrt(d_s)) if tau_s is None else float(tau_s))
 
 
-def streamkl_fwd(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, with_sum=True):
+def streamkl_fwd(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, with_sum=True, split=None):
     """Forward: returns (kl_rows, lse_t, lse_s, kl_sum), fp32 device tensors.
 
     kl_rows/lse_t/lse_s are [B, H, N_Q]; kl_sum is a 1-element tensor (None if
-    with_sum is False).  tau defaults to 1/sqrt(d) per side.
+    with_sum is False).  tau defaults to 1/sqrt(d) per side.  split: number of
+    key ranges run as separate workgroups and merged (split-K); None takes the
+    library's suggestion for the shape (1 when the GPU is already full).
     """
     import torch
     lib = load_library()
@@ -131,11 +145,64 @@ def streamkl_fwd(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, with_
     lt = torch.empty_like(kl)
     ls = torch.empty_like(kl)
     tot = torch.empty((1,), dtype=torch.float32, device=dev) if with_sum else None
+    n_split = int(lib.streamkl_fwd_split_count(B, H, n_q, n_k, int(bool(causal)))) if split is None else int(split)
+    if n_split > 1:
+        nbytes = int(lib.streamkl_fwd_split_workspace_size(B, H, n_q, n_split))
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+        code = lib.streamkl_fwd_split(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),
+                                      _dtype_code(q_t), B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s,
+                                      int(bool(causal)), n_split, ws.data_ptr(), nbytes,
+                                      kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
+                                      tot.data_ptr() if tot is not None else None, _stream_ptr(dev))
+        _check("streamkl_fwd_split", code)
+        return kl, lt, ls, tot
     code = lib.streamkl_fwd(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
                             B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, int(bool(causal)),
                             kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
                             tot.data_ptr() if tot is not None else None, _stream_ptr(dev))
     _check("streamkl_fwd", code)
+    return kl, lt, ls, tot
+
+
+STATE_FLOATS = 6
+
+
+def streamkl_fwd_partial(q_t, k_t, q_s, k_s, k_begin, k_end, tau_t=None, tau_s=None, causal=False):
+    """Partial forward over global keys [k_begin, k_end): returns the per-row
+    online states, fp32 [B, H, N_Q, 6] (see include/streamkl.h).  Partial
+    states of disjoint key ranges combine with streamkl_fwd_merge."""
+    import torch
+    lib = load_library()
+    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
+    dev = q_t.device
+    st = torch.empty((B, H, n_q, STATE_FLOATS), dtype=torch.float32, device=dev)
+    code = lib.streamkl_fwd_partial(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),
+                                    _dtype_code(q_t), B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s,
+                                    int(bool(causal)), int(k_begin), int(k_end), st.data_ptr(), _stream_ptr(dev))
+    _check("streamkl_fwd_partial", code)
+    return st
+
+
+def streamkl_fwd_merge(states, tau_t, tau_s, with_sum=True):
+    """Merge partial states [S, B, H, N_Q, 6] (or a list of [B, H, N_Q, 6])
+    into (kl_rows, lse_t, lse_s, kl_sum) as streamkl_fwd returns them."""
+    import torch
+    lib = load_library()
+    if isinstance(states, (list, tuple)):
+        states = torch.stack(list(states))
+    if states.dtype != torch.float32 or states.dim() != 5 or states.shape[-1] != STATE_FLOATS:
+        raise ValueError("states must be fp32 [S, B, H, N_Q, 6]")
+    states = states.contiguous()
+    S, B, H, n_q, _ = states.shape
+    dev = states.device
+    kl = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
+    lt, ls = torch.empty_like(kl), torch.empty_like(kl)
+    tot = torch.empty((1,), dtype=torch.float32, device=dev) if with_sum else None
+    code = lib.streamkl_fwd_merge(states.data_ptr(), S, B * H * n_q, float(tau_t), float(tau_s), kl.data_ptr(),
+                                  lt.data_ptr(), ls.data_ptr(), tot.data_ptr() if tot is not None else None,
+                                  _stream_ptr(dev))
+    _check("streamkl_fwd_merge", code)
     return kl, lt, ls, tot
 
 
@@ -239,5 +306,6 @@ def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
     return _fn_cache.apply(q_t, k_t, q_s, k_s, tau_t, tau_s, causal)
 
 
-__all__ = ["streamkl_fwd", "streamkl_bwd", "streamkl_bwd_teacher", "attention_kl", "load_library", "supported", "status_string",
+__all__ = ["streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
+           "attention_kl", "load_library", "supported", "status_string",
            "StreamKLError", "STREAMKL_F32", "STREAMKL_BF16"]

@@ -68,6 +68,8 @@ constexpr int kBf16Blocks = 8 / kWaves;
 constexpr int kTile = 32;      // MFMA tile edge; each wave owns 32 stationary items
 constexpr int kBlockX = kWaves * kTile;
 constexpr int kBN = 32;        // streamed rows per pipeline stage
+constexpr int kStateFloats = STREAMKL_STATE_FLOATS;  // (m_t, L, AT, AS, m_s, LS) per row
+constexpr int kMaxSplit = 64;  // key splits of one split forward
 
 // ---------------------------------------------------------------- type traits
 template <typename T> struct Ty;
@@ -222,6 +224,12 @@ struct FwdParams {
     bool rank_major;
     float tau_t, tau_s;
     float *kl, *lse_t, *lse_s;
+    // key range: split s of a block covers keys [k_begin + s k_chunk, that +
+    // k_chunk) within [k_begin, k_end); k_begin and k_chunk are multiples of
+    // the 32-key tile.  With state != null every (split, row) writes its raw
+    // online state there ([n_split][rows][6]) instead of the finished row.
+    int n_split, k_begin, k_end, k_chunk;
+    float *state;
 };
 
 // Scheduler group masks of __builtin_amdgcn_sched_group_barrier.
@@ -340,8 +348,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int bh, rank;
-    block_order(blockIdx.x, gridDim.x, p.nheads, p.n_qblk, p.rank_major, bh, rank);
-    const int qb = p.n_qblk - 1 - rank;  // high query blocks see the most keys under a causal mask
+    block_order(blockIdx.x, gridDim.x, p.nheads, p.n_qblk * p.n_split, p.rank_major, bh, rank);
+    const int split = rank % p.n_split;
+    const int qb = p.n_qblk - 1 - rank / p.n_split;  // high query blocks see the most keys under a causal mask
     const int hh = bh % p.H, bb = bh / p.H;
     const T *Qt = static_cast<const T *>(p.q_t) + bb * p.st[0] + hh * p.st[1];
     const T *Kt = static_cast<const T *>(p.k_t) + bb * p.st[3] + hh * p.st[4];
@@ -358,16 +367,22 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     const int qlast_w = min(n_q - 1, q0w + kTile - 1);
 
     const int qlast_wg = min(n_q - 1, qb * kBlockX + kBlockX - 1);
-    const int kend = CAUSAL ? min(n_k, qlast_wg + off + 1) : n_k;
-    const int ntile = (kend + kBN - 1) / kBN;
-    auto active = [&](int t) { return wave_live && (!CAUSAL || t * kBN <= qlast_w + off); };
-    auto need_mask = [&](int t) { return (t * kBN + kBN > n_k) || (CAUSAL && t * kBN + kBN - 1 > q0w + off); };
+    // this block's keys: its split's range, cut at the causal end of its queries
+    const int kb0 = p.k_begin + split * p.k_chunk;
+    const int kend = min(min(p.k_end, kb0 + p.k_chunk), CAUSAL ? min(n_k, qlast_wg + off + 1) : n_k);
+    const int ntile = kend > kb0 ? (kend - kb0 + kBN - 1) / kBN : 0;
+    const int t0 = kb0 / kBN;  // tile t of the loop is global key tile t0 + t
+    auto active = [&](int t) { return wave_live && (!CAUSAL || (t0 + t) * kBN <= qlast_w + off); };
+    auto need_mask = [&](int t) {
+        const int k0 = (t0 + t) * kBN;
+        return (k0 + kBN > n_k) || (CAUSAL && k0 + kBN - 1 > q0w + off);
+    };
     auto issue = [&](int t, char *stage) {
-        dma_tile<T, DT>(Kt, skt, t * kBN, n_k, stage, w, lane);
-        dma_tile<T, DS>(Ks, sks, t * kBN, n_k, stage + TileT::kBytes, w, lane);
+        dma_tile<T, DT>(Kt, skt, (t0 + t) * kBN, n_k, stage, w, lane);
+        dma_tile<T, DS>(Ks, sks, (t0 + t) * kBN, n_k, stage + TileT::kBytes, w, lane);
     };
 
-    issue(0, smem);
+    if (ntile > 0) issue(0, smem);
     if (ntile > 1) issue(1, smem + STAGE);
 
     u32x4 qtv[span_vecs<T, DT>()], qsv[span_vecs<T, DS>()];
@@ -379,7 +394,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
 
     dma_barrier();
     f32x16 xt0 = {}, xs0 = {}, xt1 = {}, xs1 = {};
-    if (active(0)) {
+    if (ntile > 0 && active(0)) {
         xt0 = tile_scores<T, DT>(smem, qtv, l32, hf);
         xs0 = tile_scores<T, DS>(smem + TileT::kBytes, qsv, l32, hf);
     }
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
         const bool a_nxt = it + 1 < ntile && active(it + 1);
         const bool m_cur = need_mask(it);
         const char *bn = smem + ((it + 1) & 1) * STAGE;
-        const int k0 = it * kBN;
+        const int k0 = (t0 + it) * kBN;
         if (a_cur && a_nxt && !m_cur) {
             nxt_t = tile_scores<T, DT>(bn, qtv, l32, hf);
             nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, qsv, l32, hf);
@@ -436,15 +451,58 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     const float v1 = fast_exp2(cs * (o.ms - mS)), v2 = fast_exp2(cs * (ms2 - mS));
     const float LS = o.ls * v1 + ls2 * v2;
     if (hf == 0 && qv) {
-        const float lse_t = p.tau_t * m + logf(L);
-        const float lse_s = p.tau_s * mS + logf(LS);
-        // E_{P_t}[s_t - s_s] - LSE_t + LSE_s
-        const float kl = (p.tau_t * AT - p.tau_s * AS) / L - lse_t + lse_s;
         const int64_t row = ((int64_t)bb * p.H + hh) * n_q + q;
-        p.kl[row] = kl;
-        p.lse_t[row] = lse_t;
-        p.lse_s[row] = lse_s;
+        if (p.state) {
+            float *o6 = p.state + ((int64_t)split * p.nheads * n_q + row) * kStateFloats;
+            o6[0] = m;
+            o6[1] = L;
+            o6[2] = AT;
+            o6[3] = AS;
+            o6[4] = mS;
+            o6[5] = LS;
+        } else {
+            const float lse_t = p.tau_t * m + logf(L);
+            const float lse_s = p.tau_s * mS + logf(LS);
+            // E_{P_t}[s_t - s_s] - LSE_t + LSE_s
+            const float kl = (p.tau_t * AT - p.tau_s * AS) / L - lse_t + lse_s;
+            p.kl[row] = kl;
+            p.lse_t[row] = lse_t;
+            p.lse_s[row] = lse_s;
+        }
     }
+}
+
+// Merge of partial online states.  Each of n_states states of a row holds, for
+// its own key subset, reference maxima m_t, m_s of the raw scores and
+//   L = sum 2^(c_t (x_t - m_t)),  AT = sum 2^(c_t (x_t - m_t)) x_t,
+//   AS = sum 2^(c_t (x_t - m_t)) x_s,  LS = sum 2^(c_s (x_s - m_s))
+// (c = tau log2 e).  Rescaled to the largest references they add up to the
+// state of the union, which finishes into LSE_t, LSE_s and the row's KL.
+__global__ __launch_bounds__(256) void streamkl_merge_kernel(const float *st, int n_states, int64_t rows,
+                                                             float tau_t, float tau_s, float *kl_rows,
+                                                             float *lse_t, float *lse_s) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows) return;
+    const float ct = tau_t * kLog2e, cs = tau_s * kLog2e;
+    float m = kMasked, L = 0.f, AT = 0.f, AS = 0.f, mS = kMasked, LS = 0.f;
+    for (int k = 0; k < n_states; ++k) {
+        const float *o = st + ((int64_t)k * rows + row) * kStateFloats;
+        const float m2 = o[0], L2 = o[1], AT2 = o[2], AS2 = o[3], mS2 = o[4], LS2 = o[5];
+        const float mn = fmaxf(m, m2);
+        const float w1 = fast_exp2(ct * (m - mn)), w2 = fast_exp2(ct * (m2 - mn));
+        L = L * w1 + L2 * w2;
+        AT = AT * w1 + AT2 * w2;
+        AS = AS * w1 + AS2 * w2;
+        m = mn;
+        const float mSn = fmaxf(mS, mS2);
+        LS = LS * fast_exp2(cs * (mS - mSn)) + LS2 * fast_exp2(cs * (mS2 - mSn));
+        mS = mSn;
+    }
+    const float lt = tau_t * m + logf(L);
+    const float ls = tau_s * mS + logf(LS);
+    kl_rows[row] = (tau_t * AT - tau_s * AS) / L - lt + ls;
+    lse_t[row] = lt;
+    lse_s[row] = ls;
 }
 
 // Deterministic sum of n fp32 values, one block: each thread accumulates a
@@ -1052,6 +1110,51 @@ bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool gs, bool first) {
     return nullptr;
 }
 
+// The forward over keys [k_begin, k_end) in n_split equal chunks: finished
+// rows (state == null, one chunk) or raw online states ([n_split][rows][6]).
+streamkl_status fwd_common(const void *q_t, const void *k_t, const void *q_s, const void *k_s, streamkl_dtype dtype,
+                           int B, int H, int n_q, int n_k, int d_t, int d_s, const int64_t *strides, float tau_t,
+                           float tau_s, int causal, int k_begin, int k_end, int n_split, float *state,
+                           float *kl_rows, float *lse_t, float *lse_s, float *kl_sum, void *stream) {
+    const Shape s{B, H, n_q, n_k, d_t, d_s};
+    FwdParams p{};
+    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, p.st);
+    if (rc != STREAMKL_OK) return rc;
+    p.q_t = q_t; p.k_t = k_t; p.q_s = q_s; p.k_s = k_s;
+    p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
+    p.n_qblk = (n_q + kBlockX - 1) / kBlockX;
+    if ((int64_t)B * H * p.n_qblk * n_split * kThreads > (int64_t)UINT32_MAX) return STREAMKL_ERR_INVALID;
+    {
+        int64_t mn = INT64_MAX, mx = 0, tot = 0;
+        for (int qb = 0; qb < p.n_qblk; ++qb) {
+            const int64_t t = fwd_block_tiles(s, causal, qb);
+            mn = std::min(mn, t);
+            mx = std::max(mx, t);
+            tot += t;
+        }
+        p.rank_major = want_rank_major(mn, mx, tot, p.nheads);
+    }
+    p.tau_t = tau_t; p.tau_s = tau_s;
+    p.kl = kl_rows; p.lse_t = lse_t; p.lse_s = lse_s;
+    p.n_split = n_split;
+    p.k_begin = k_begin;
+    p.k_end = k_end;
+    const int per = (k_end - k_begin + n_split - 1) / n_split;
+    p.k_chunk = ((per + kBN - 1) / kBN) * kBN;
+    p.state = state;
+    fwd_launch_t fn = dtype == STREAMKL_BF16 ? pick_fwd1<bf16_t>(d_t, d_s, causal) : pick_fwd1<float>(d_t, d_s, causal);
+    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    fn(p, B * H * p.n_qblk * n_split, hs);
+    if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    if (kl_sum && !state) {
+        hipLaunchKernelGGL(streamkl_sum_kernel, dim3(1), dim3(1024), 0, hs, (const float *)kl_rows,
+                           (int64_t)B * H * n_q, kl_sum);
+        if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    }
+    return STREAMKL_OK;
+}
+
 // Both backward entry points: gradients of sum_r g_r KL_r with respect to the
 // student (first = false, outputs d_s wide) or the teacher (first = true,
 // outputs d_t wide, needs the forward's per-row KL).
@@ -1144,35 +1247,71 @@ streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, 
                              streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
                              const int64_t *strides, float tau_t, float tau_s, int causal, float *kl_rows,
                              float *lse_t, float *lse_s, float *kl_sum, void *stream) {
-    const Shape s{B, H, n_q, n_k, d_t, d_s};
-    FwdParams p{};
-    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, p.st);
-    if (rc != STREAMKL_OK) return rc;
     if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
-    p.q_t = q_t; p.k_t = k_t; p.q_s = q_s; p.k_s = k_s;
-    p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
-    p.n_qblk = (n_q + kBlockX - 1) / kBlockX;
-    {
-        int64_t mn = INT64_MAX, mx = 0, tot = 0;
-        for (int qb = 0; qb < p.n_qblk; ++qb) {
-            const int64_t t = fwd_block_tiles(s, causal, qb);
-            mn = std::min(mn, t);
-            mx = std::max(mx, t);
-            tot += t;
-        }
-        p.rank_major = want_rank_major(mn, mx, tot, p.nheads);
-    }
-    p.tau_t = tau_t; p.tau_s = tau_s;
-    p.kl = kl_rows; p.lse_t = lse_t; p.lse_s = lse_s;
-    fwd_launch_t fn = dtype == STREAMKL_BF16 ? pick_fwd1<bf16_t>(d_t, d_s, causal) : pick_fwd1<float>(d_t, d_s, causal);
-    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+    return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, 0, n_k,
+                      1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
+}
+
+int streamkl_fwd_split_count(int B, int H, int n_q, int n_k, int causal) {
+    (void)causal;
+    if (B < 1 || H < 1 || n_q < 1 || n_k < 1) return 1;
+    // aim at two workgroups per CU twice over (256 CUs); keep >= 16 key tiles per split
+    const int64_t base = (int64_t)B * H * ((n_q + kBlockX - 1) / kBlockX);
+    const int64_t want = 2 * 2 * 256;
+    if (base >= want) return 1;
+    int64_t n = (want + base - 1) / base;
+    n = std::min<int64_t>(n, std::max<int64_t>(1, n_k / (16 * kBN)));
+    return (int)std::min<int64_t>(n, kMaxSplit);
+}
+
+size_t streamkl_fwd_split_workspace_size(int B, int H, int n_q, int n_split) {
+    if (B < 1 || H < 1 || n_q < 1 || n_split < 1) return 0;
+    return (size_t)n_split * B * H * n_q * kStateFloats * sizeof(float);
+}
+
+streamkl_status streamkl_fwd_split(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                   streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                   const int64_t *strides, float tau_t, float tau_s, int causal, int n_split,
+                                   void *workspace, size_t workspace_bytes, float *kl_rows, float *lse_t,
+                                   float *lse_s, float *kl_sum, void *stream) {
+    if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
+    if (n_split < 1 || n_split > kMaxSplit) return STREAMKL_ERR_INVALID;
+    if (n_split == 1)
+        return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, 0,
+                          n_k, 1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
+    if (B < 1 || H < 1 || n_q < 1) return STREAMKL_ERR_INVALID;
+    if (!workspace || ((uintptr_t)workspace) % 16 != 0) return STREAMKL_ERR_INVALID;
+    if (workspace_bytes < streamkl_fwd_split_workspace_size(B, H, n_q, n_split)) return STREAMKL_ERR_WORKSPACE;
+    float *state = static_cast<float *>(workspace);
+    streamkl_status rc = fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s,
+                                    causal, 0, n_k, n_split, state, nullptr, nullptr, nullptr, nullptr, stream);
+    if (rc != STREAMKL_OK) return rc;
+    return streamkl_fwd_merge(state, n_split, (int64_t)B * H * n_q, tau_t, tau_s, kl_rows, lse_t, lse_s, kl_sum,
+                              stream);
+}
+
+streamkl_status streamkl_fwd_partial(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                     streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                     const int64_t *strides, float tau_t, float tau_s, int causal, int k_begin,
+                                     int k_end, float *state, void *stream) {
+    if (!state || ((uintptr_t)state) % 16 != 0) return STREAMKL_ERR_INVALID;
+    if (k_begin < 0 || k_end > n_k || k_begin >= k_end) return STREAMKL_ERR_INVALID;
+    if (k_begin % kBN != 0 || (k_end % kBN != 0 && k_end != n_k)) return STREAMKL_ERR_INVALID;
+    return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, k_begin,
+                      k_end, 1, state, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+streamkl_status streamkl_fwd_merge(const float *states, int n_states, int64_t rows, float tau_t, float tau_s,
+                                   float *kl_rows, float *lse_t, float *lse_s, float *kl_sum, void *stream) {
+    if (!states || !kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
+    if (n_states < 1 || rows < 1 || (rows + 255) / 256 > (int64_t)INT32_MAX) return STREAMKL_ERR_INVALID;
+    if (!(tau_t >= 0.f) || !(tau_s >= 0.f) || !isfinite(tau_t) || !isfinite(tau_s)) return STREAMKL_ERR_INVALID;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const int grid = B * H * p.n_qblk;
-    fn(p, grid, hs);
+    hipLaunchKernelGGL(streamkl_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, hs, states,
+                       n_states, rows, tau_t, tau_s, kl_rows, lse_t, lse_s);
     if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
     if (kl_sum) {
-        hipLaunchKernelGGL(streamkl_sum_kernel, dim3(1), dim3(1024), 0, hs, (const float *)kl_rows,
-                           (int64_t)B * H * n_q, kl_sum);
+        hipLaunchKernelGGL(streamkl_sum_kernel, dim3(1), dim3(1024), 0, hs, (const float *)kl_rows, rows, kl_sum);
         if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
     }
     return STREAMKL_OK;

@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--no-baseline-mem", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    ap.add_argument("--split", type=int, default=None,
+                    help="key splits of the forward (default: the library's suggestion for the shape)")
     ap.add_argument("--teacher-grads", action="store_true",
                     help="also time the first-argument (teacher) backward, outside the headline step")
     args = ap.parse_args()
@@ -187,10 +189,20 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
+    # split-K forward when the library suggests it for this shape (small launches)
+    n_split = lib.streamkl_fwd_split_count(B, H, w.n_q, w.n_k, int(w.causal)) if args.split is None else args.split
+    ws_bytes = lib.streamkl_fwd_split_workspace_size(B, H, w.n_q, n_split) if n_split > 1 else 0
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+
     def fwd():
-        rc = lib.streamkl_fwd(ptr["q_t"], ptr["k_t"], ptr["q_s"], ptr["k_s"], code, B, H, w.n_q, w.n_k, w.d_t, w.d_s,
-                              None, w.tau_t, w.tau_s, int(w.causal), kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
-                              tot.data_ptr(), sp)
+        if n_split > 1:
+            rc = lib.streamkl_fwd_split(ptr["q_t"], ptr["k_t"], ptr["q_s"], ptr["k_s"], code, B, H, w.n_q, w.n_k,
+                                        w.d_t, w.d_s, None, w.tau_t, w.tau_s, int(w.causal), n_split, ws.data_ptr(),
+                                        ws_bytes, kl.data_ptr(), lt.data_ptr(), ls.data_ptr(), tot.data_ptr(), sp)
+        else:
+            rc = lib.streamkl_fwd(ptr["q_t"], ptr["k_t"], ptr["q_s"], ptr["k_s"], code, B, H, w.n_q, w.n_k, w.d_t,
+                                  w.d_s, None, w.tau_t, w.tau_s, int(w.causal), kl.data_ptr(), lt.data_ptr(),
+                                  ls.data_ptr(), tot.data_ptr(), sp)
         if rc:
             raise RuntimeError(skl.status_string(rc))
 
@@ -250,7 +262,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "n_q": w.n_q, "n_k": w.n_k, "d_t": w.d_t, "d_s": w.d_s,
-                   "causal": w.causal, "inputs": f"seeded {w.recipe} N(0,1)", "parallelism": "single GPU"},
+                   "causal": w.causal, "inputs": f"seeded {w.recipe} N(0,1)", "parallelism": "single GPU",
+                   "fwd_key_splits": int(n_split)},
         "pct_peak": round(100.0 * value / peak, 2),
         "fwd_ms": round(float(np.mean(t_f)), 4), "bwd_ms": round(float(np.mean(t_b)), 4),
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),

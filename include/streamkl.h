@@ -57,7 +57,7 @@ typedef enum {
                                      or a problem too large for one dispatch (B H (ceil(n_q/128) +
                                      ceil(n_k/128)) 256 >= 2^32, or n_q / n_k beyond 2^30 - 128) */
     STREAMKL_ERR_UNSUPPORTED = 2, /* (dtype, d_t, d_s) combination not built */
-    STREAMKL_ERR_WORKSPACE = 3,   /* reserved: workspace too small */
+    STREAMKL_ERR_WORKSPACE = 3,   /* workspace too small (streamkl_fwd_split) */
     STREAMKL_ERR_HIP = 4          /* a HIP launch error was reported */
 } streamkl_status;
 
@@ -90,6 +90,60 @@ streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, 
                              const int64_t *strides, float tau_t, float tau_s, int causal,
                              float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
                              void *stream);
+
+/*
+ * Split forward and its pieces.  The per-row online state has an associative
+ * merge, so the forward can run over disjoint key ranges independently and be
+ * combined afterwards: within one GPU to fill it when B H ceil(n_q / 128) is
+ * small (split-K), across GPUs when the keys are sharded (context parallel).
+ *
+ * A row's partial state over a key subset J is STREAMKL_STATE_FLOATS floats
+ *   [m_t, L, AT, AS, m_s, LS]
+ * with reference values m_t, m_s (raw scores q.k; any finite value that keeps
+ * the sums in range -- the kernels use them as running references), c = tau
+ * log2(e), and over the allowed keys j in J
+ *   L = sum 2^(c_t (x_t[j] - m_t)),  AT = sum 2^(c_t (x_t[j] - m_t)) x_t[j],
+ *   AS = sum 2^(c_t (x_t[j] - m_t)) x_s[j],  LS = sum 2^(c_s (x_s[j] - m_s)),
+ * x = q . k unscaled.  An empty subset has L = LS = 0.  The union of subsets
+ * merges by rescaling to the larger references and adding; the finish is
+ *   LSE_t = tau_t m_t + ln L,  LSE_s = tau_s m_s + ln LS,
+ *   KL = (tau_t AT - tau_s AS) / L - LSE_t + LSE_s.
+ */
+#define STREAMKL_STATE_FLOATS 6
+
+/* Partial forward over the keys [k_begin, k_end) (global key indices; the
+ * causal mask, if any, is taken in global coordinates).  k_begin must be a
+ * multiple of 32 and k_end a multiple of 32 or n_k.  state: out, device fp32
+ * [B*H*n_q][STREAMKL_STATE_FLOATS], 16-byte aligned.  Other arguments as
+ * streamkl_fwd. */
+streamkl_status streamkl_fwd_partial(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                     streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                     const int64_t *strides, float tau_t, float tau_s, int causal,
+                                     int k_begin, int k_end, float *state, void *stream);
+
+/* Merge of n_states partial states per row, laid out [n_states][rows][6]
+ * (device fp32), into kl_rows, lse_t, lse_s ([rows] fp32, as streamkl_fwd)
+ * and, if kl_sum is not NULL, their deterministic sum. */
+streamkl_status streamkl_fwd_merge(const float *states, int n_states, int64_t rows, float tau_t, float tau_s,
+                                   float *kl_rows, float *lse_t, float *lse_s, float *kl_sum, void *stream);
+
+/* Suggested number of key splits for streamkl_fwd_split on an MI355X (1 when
+ * the unsplit forward already fills the GPU). */
+int streamkl_fwd_split_count(int B, int H, int n_q, int n_k, int causal);
+
+/* Workspace bytes streamkl_fwd_split needs: n_split * B * H * n_q * 6 * 4. */
+size_t streamkl_fwd_split_workspace_size(int B, int H, int n_q, int n_split);
+
+/* streamkl_fwd with the keys cut into n_split (1..64) equal ranges, one
+ * launch over all of them (their states in the caller's workspace, 16-byte
+ * aligned, at least streamkl_fwd_split_workspace_size bytes, else
+ * STREAMKL_ERR_WORKSPACE), then the merge.  Same outputs as streamkl_fwd up to
+ * rounding. */
+streamkl_status streamkl_fwd_split(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                   streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                   const int64_t *strides, float tau_t, float tau_s, int causal, int n_split,
+                                   void *workspace, size_t workspace_bytes, float *kl_rows, float *lse_t,
+                                   float *lse_s, float *kl_sum, void *stream);
 
 /*
  * Backward.  Gradients of L = sum_r g_r KL_r with respect to the student

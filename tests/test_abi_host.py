@@ -129,3 +129,42 @@ def test_bwd_teacher_rejects_bad_arguments_before_any_hip_call():
     assert call(causal=1) == INV
     assert call(d_t=32) == UNS
     assert call(tau_t=-0.5) == INV
+
+
+def test_split_forward_pieces_reject_bad_arguments_before_any_hip_call():
+    lib = skl.load_library()
+    base = dict(q_t=A, k_t=A + 0x100000, q_s=A + 0x200000, k_s=A + 0x300000, dtype=skl.STREAMKL_BF16,
+                B=2, H=3, n_q=100, n_k=300, d_t=128, d_s=64, tau_t=0.088, tau_s=0.125, causal=0)
+
+    def partial(k0, k1, st=A + 0x400000, **kw):
+        a = dict(base); a.update(kw)
+        return lib.streamkl_fwd_partial(a["q_t"], a["k_t"], a["q_s"], a["k_s"], a["dtype"], a["B"], a["H"],
+                                        a["n_q"], a["n_k"], a["d_t"], a["d_s"], None, a["tau_t"], a["tau_s"],
+                                        a["causal"], k0, k1, st, None)
+    assert partial(16, 64) == INV       # k_begin not a multiple of 32
+    assert partial(0, 70) == INV        # k_end neither a multiple of 32 nor n_k
+    assert partial(64, 64) == INV       # empty range
+    assert partial(0, 301) == INV       # beyond n_k
+    assert partial(0, 64, st=None) == INV
+    assert partial(0, 64, st=A + 4) == INV
+    assert partial(0, 64, d_t=48) == UNS
+
+    def split(n, ws=A + 0x500000, nbytes=1 << 30, **kw):
+        a = dict(base); a.update(kw)
+        return lib.streamkl_fwd_split(a["q_t"], a["k_t"], a["q_s"], a["k_s"], a["dtype"], a["B"], a["H"],
+                                      a["n_q"], a["n_k"], a["d_t"], a["d_s"], None, a["tau_t"], a["tau_s"],
+                                      a["causal"], n, ws, nbytes, A + 0x600000, A + 0x700000, A + 0x800000, None,
+                                      None)
+    need = lib.streamkl_fwd_split_workspace_size(2, 3, 100, 4)
+    assert need == 4 * 2 * 3 * 100 * 6 * 4
+    assert split(4, nbytes=need - 1) == skl.STREAMKL_ERR_WORKSPACE
+    assert split(4, ws=None) == INV
+    assert split(0) == INV and split(65) == INV
+    assert split(4, tau_s=-1.0) == INV
+    assert lib.streamkl_fwd_merge(None, 2, 100, 0.1, 0.1, A, A, A, None, None) == INV
+    assert lib.streamkl_fwd_merge(A, 0, 100, 0.1, 0.1, A, A, A, None, None) == INV
+    assert lib.streamkl_fwd_merge(A, 2, 0, 0.1, 0.1, A, A, A, None, None) == INV
+    # the suggested split count: 1 when the unsplit forward fills the GPU, more for small launches
+    assert lib.streamkl_fwd_split_count(2, 16, 16384, 16384, 0) == 1
+    assert lib.streamkl_fwd_split_count(4, 12, 2048, 2048, 0) == 2
+    assert lib.streamkl_fwd_split_count(1, 1, 128, 128, 0) == 1

@@ -70,7 +70,7 @@ def test_no_spills_in_the_mfma_loops(asm):
     text = "\n".join(asm)
     found = list(re.finditer(r"\.name:\s+(_ZN12_GLOBAL__N_1\d+streamkl_\w+)[\s\S]*?"
                              r"\.private_segment_fixed_size:\s+(\d+)", text))
-    assert len(found) == 65  # 64 forward/backward instantiations + the sum kernel
+    assert len(found) == 66  # 64 forward/backward instantiations + the sum and merge kernels
     for m in found:
         assert int(m.group(2)) <= 64, m.group(1)
     for name, body in _kernels(asm):
