@@ -52,6 +52,10 @@ def _load():
     lib.oracle_dqt_rows.restype = None
     lib.oracle_dkt_keys.argtypes = common + [ctypes.c_void_p, _D, _I, _I, _I, _i64p, _f64p]
     lib.oracle_dkt_keys.restype = None
+    lib.oracle_vocab_fwd.argtypes = [_f64p, _f64p, _I, _I, _D, _f64p, _f64p, _f64p, ctypes.POINTER(ctypes.c_double)]
+    lib.oracle_vocab_fwd.restype = None
+    lib.oracle_vocab_bwd.argtypes = [_f64p, _f64p, _I, _I, _D, ctypes.c_void_p, _D, _f64p, ctypes.c_void_p]
+    lib.oracle_vocab_bwd.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = _I
     _lib = lib
@@ -185,3 +189,44 @@ def dkt_keys(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, b, h, keys, g=None):
     lib.oracle_dkt_keys(*arrs, B, H, n_q, n_k, d_t, d_s, float(tau_t), float(tau_s), int(causal),
                         gp, gs, int(b), int(h), keys.size, keys, out)
     return out
+
+
+def _vocab_prep(z_t, z_s):
+    z_t = np.ascontiguousarray(z_t, dtype=np.float64)
+    z_s = np.ascontiguousarray(z_s, dtype=np.float64)
+    if z_t.shape != z_s.shape or z_t.ndim < 1:
+        raise ValueError("z_t and z_s must share a shape [..., V]")
+    V = z_t.shape[-1]
+    return z_t.reshape(-1, V), z_s.reshape(-1, V), z_t.shape
+
+
+def vocab_fwd(z_t, z_s, temperature=1.0):
+    """Per-row KL(softmax(z_t / T) || softmax(z_s / T)), LSE_t, LSE_s of the
+    scaled logits (shape [...] of the leading dims) and their compensated sum."""
+    lib = _load()
+    zt, zs, shape = _vocab_prep(z_t, z_s)
+    rows, V = zt.shape
+    kl = np.empty(rows); lt = np.empty(rows); ls = np.empty(rows)
+    tot = ctypes.c_double(0.0)
+    lib.oracle_vocab_fwd(zt, zs, rows, V, 1.0 / float(temperature), kl, lt, ls, ctypes.byref(tot))
+    lead = shape[:-1]
+    return kl.reshape(lead), lt.reshape(lead), ls.reshape(lead), tot.value
+
+
+def vocab_bwd(z_t, z_s, temperature=1.0, g=None, teacher=False):
+    """dz_s (and dz_t if teacher) of L = sum_r g_r KL_r; g None means g_r = 1."""
+    lib = _load()
+    zt, zs, shape = _vocab_prep(z_t, z_s)
+    rows, V = zt.shape
+    if g is None or np.isscalar(g):
+        garr, gs = None, float(1.0 if g is None else g)
+    else:
+        garr = np.ascontiguousarray(g, dtype=np.float64).reshape(-1)
+        if garr.size != rows:
+            raise ValueError("g must have one value per row")
+        gs = 0.0
+    dzs = np.empty((rows, V))
+    dzt = np.empty((rows, V)) if teacher else None
+    lib.oracle_vocab_bwd(zt, zs, rows, V, 1.0 / float(temperature), garr.ctypes.data if garr is not None else None,
+                         gs, dzs, dzt.ctypes.data if dzt is not None else None)
+    return (dzs.reshape(shape), dzt.reshape(shape)) if teacher else dzs.reshape(shape)

@@ -27,7 +27,10 @@
  *  - gradients are for L = sum_r g_r * KL_r with respect to the student
  *    queries and keys (the teacher is a fixed target); the *_teacher and
  *    *_dqt / *_dkt functions give the same loss's gradients with respect to the
- *    teacher (first-argument) queries and keys.
+ *    teacher (first-argument) queries and keys;
+ *  - oracle_vocab_fwd / oracle_vocab_bwd apply the same definition to rows of
+ *    vocabulary logits (section 3.1 at temperature T, scale = 1/T); the T^2
+ *    factor of section 3.3 is left to the caller.
  *
  * Layout: every tensor is contiguous [B][H][N][d] of fp64 values (bf16 and
  * fp32 inputs are passed already widened, which is exact); outputs are fp64.
@@ -538,6 +541,89 @@ void oracle_dkt_keys(const double *q_t, const double *k_t, const double *q_s, co
         free(ss);
         free(dS);
         free(part);
+    }
+}
+
+/*
+ * Vocabulary-logit KL ("Lecture 05 - Where It All Lands", section 3.1: the
+ * distillation loss at temperature T between the teacher and student output
+ * distributions over the vocabulary; section 3.3: any T^2 factor is the
+ * caller's).  Per row r of zt, zs ([rows][V]):
+ *   p = softmax(scale * zt[r]),  q = softmax(scale * zs[r]),  scale = 1 / T
+ *   KL_r = sum_v p[v] (log p[v] - log q[v])   (log domain, as row_kl)
+ * kl_sum: Neumaier-compensated sum of the rows.
+ */
+void oracle_vocab_fwd(const double *zt, const double *zs, int rows, int V, double scale,
+                      double *kl_rows, double *lse_t, double *lse_s, double *kl_sum)
+{
+#pragma omp parallel
+    {
+        double *st = (double *)malloc(sizeof(double) * (size_t)V);
+        double *ss = (double *)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 4)
+        for (int r = 0; r < rows; ++r) {
+            for (int v = 0; v < V; ++v) {
+                st[v] = scale * zt[(size_t)r * V + v];
+                ss[v] = scale * zs[(size_t)r * V + v];
+            }
+            double lt = log_sum_exp(st, V), ls = log_sum_exp(ss, V), acc = 0.0;
+            for (int v = 0; v < V; ++v) {
+                double lp = st[v] - lt, lq = ss[v] - ls, p = exp(lp);
+                if (p != 0.0)
+                    acc += p * (lp - lq);
+            }
+            kl_rows[r] = acc;
+            lse_t[r] = lt;
+            lse_s[r] = ls;
+        }
+        free(st);
+        free(ss);
+    }
+    double s = 0.0, c = 0.0;
+    for (int r = 0; r < rows; ++r) {
+        double x = kl_rows[r], t = s + x;
+        if (fabs(s) >= fabs(x)) c += (s - t) + x;
+        else c += (x - t) + s;
+        s = t;
+    }
+    *kl_sum = s + c;
+}
+
+/*
+ * Gradients of L = sum_r g_r KL_r with respect to the logits:
+ *   dzs[r][v] = g_r * scale * (q[v] - p[v])
+ *   dzt[r][v] = g_r * scale * p[v] (log p[v] - log q[v] - KL_r)   (if dzt != NULL)
+ * (the derivations of row_dS and row_dS_teacher with s = scale * z).
+ */
+void oracle_vocab_bwd(const double *zt, const double *zs, int rows, int V, double scale,
+                      const double *g_rows, double g_scalar, double *dzs, double *dzt)
+{
+#pragma omp parallel
+    {
+        double *st = (double *)malloc(sizeof(double) * (size_t)V);
+        double *ss = (double *)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 4)
+        for (int r = 0; r < rows; ++r) {
+            double g = g_rows ? g_rows[r] : g_scalar;
+            for (int v = 0; v < V; ++v) {
+                st[v] = scale * zt[(size_t)r * V + v];
+                ss[v] = scale * zs[(size_t)r * V + v];
+            }
+            double lt = log_sum_exp(st, V), ls = log_sum_exp(ss, V), kl = 0.0;
+            for (int v = 0; v < V; ++v) {
+                double lp = st[v] - lt, lq = ss[v] - ls, p = exp(lp);
+                if (p != 0.0)
+                    kl += p * (lp - lq);
+            }
+            for (int v = 0; v < V; ++v) {
+                double lp = st[v] - lt, lq = ss[v] - ls, p = exp(lp), q = exp(lq);
+                dzs[(size_t)r * V + v] = g * scale * (q - p);
+                if (dzt)
+                    dzt[(size_t)r * V + v] = p != 0.0 ? g * scale * p * (lp - lq - kl) : 0.0;
+            }
+        }
+        free(st);
+        free(ss);
     }
 }
 
