@@ -64,6 +64,13 @@ def load_library():
     lib.streamkl_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, i, vp, sz, vp, vp, vp,
                                        vp, vp]
     lib.streamkl_fwd_split.restype = i
+    i64 = ctypes.c_int64
+    lib.streamkl_vocab_fwd.argtypes = [vp, vp, i, i64, i, i64, i64, f, vp, vp, vp, vp, vp]
+    lib.streamkl_vocab_fwd.restype = i
+    lib.streamkl_vocab_bwd.argtypes = [vp, vp, i, i64, i, i64, i64, f, vp, vp, vp, vp, f, vp, vp, vp]
+    lib.streamkl_vocab_bwd.restype = i
+    lib.streamkl_vocab_fwd_bwd.argtypes = [vp, vp, i, i64, i, i64, i64, f, vp, f, vp, vp, vp, vp, vp, vp, vp]
+    lib.streamkl_vocab_fwd_bwd.restype = i
     lib.streamkl_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.streamkl_bwd_workspace_size.restype = ctypes.c_size_t
     lib.streamkl_status_string.argtypes = [i]
@@ -259,6 +266,112 @@ def streamkl_bwd_teacher(q_t, k_t, q_s, k_s, lse_t, lse_s, kl_rows, grad_rows=No
     return dq, dk
 
 
+def _vocab_rows(z_t, z_s):
+    """Flatten [..., V] logits to rows; returns (zt2, zs2, lead_shape, rows, V, ld_t, ld_s)."""
+    import torch
+    for t in (z_t, z_s):
+        if not isinstance(t, torch.Tensor) or t.dim() < 1:
+            raise ValueError("z_t and z_s must be tensors [..., V]")
+        if t.device.type != "cuda":
+            raise ValueError("logits must be device (HIP) tensors")
+    if z_t.dtype != z_s.dtype or z_t.device != z_s.device:
+        raise ValueError("z_t and z_s must share dtype and device")
+    if tuple(z_t.shape) != tuple(z_s.shape):
+        raise ValueError("z_t and z_s must have the same shape [..., V]")
+    V = z_t.shape[-1]
+    lead = tuple(z_t.shape[:-1])
+    zt2 = z_t.reshape(-1, V)  # a view when the rows share one stride, else a copy
+    zs2 = z_s.reshape(-1, V)
+    if zt2.stride(-1) != 1:
+        zt2 = zt2.contiguous()
+    if zs2.stride(-1) != 1:
+        zs2 = zs2.contiguous()
+    rows = zt2.shape[0]
+    ld_t = zt2.stride(0) if rows > 1 else V
+    ld_s = zs2.stride(0) if rows > 1 else V
+    return zt2, zs2, lead, rows, V, ld_t, ld_s
+
+
+def _row_vec(name, t, rows, dev, lead):
+    import torch
+    if t.dtype != torch.float32 or t.device != dev or t.numel() != rows or tuple(t.shape) != lead:
+        raise ValueError(f"{name} must be an fp32 tensor of shape {lead} on the logits' device")
+    return t.contiguous()
+
+
+def streamkl_vocab_fwd(z_t, z_s, temperature=1.0, with_sum=True):
+    """Per-row KL(softmax(z_t / T) || softmax(z_s / T)) over the last dim.
+
+    Returns (kl_rows, lse_t, lse_s, kl_sum): fp32 tensors of the leading shape
+    and a 1-element sum (None if with_sum is False)."""
+    import torch
+    lib = load_library()
+    zt, zs, lead, rows, V, ld_t, ld_s = _vocab_rows(z_t, z_s)
+    dev = zt.device
+    kl = torch.empty(lead, dtype=torch.float32, device=dev)
+    lt, ls = torch.empty_like(kl), torch.empty_like(kl)
+    tot = torch.empty((1,), dtype=torch.float32, device=dev) if with_sum else None
+    code = lib.streamkl_vocab_fwd(zt.data_ptr(), zs.data_ptr(), _dtype_code(zt), rows, V, ld_t, ld_s,
+                                  float(temperature), kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
+                                  tot.data_ptr() if tot is not None else None, _stream_ptr(dev))
+    _check("streamkl_vocab_fwd", code)
+    return kl, lt, ls, tot
+
+
+def streamkl_vocab_bwd(z_t, z_s, lse_t, lse_s, kl_rows=None, temperature=1.0, grad_rows=None, grad_scalar=1.0,
+                       teacher=False):
+    """Gradients of L = sum_r g_r KL_r: dz_s, or (dz_s, dz_t) if teacher
+    (then kl_rows, the forward's, is needed).  Same shape and dtype as z_s."""
+    import torch
+    lib = load_library()
+    zt, zs, lead, rows, V, ld_t, ld_s = _vocab_rows(z_t, z_s)
+    dev = zt.device
+    lse_t = _row_vec("lse_t", lse_t, rows, dev, lead)
+    lse_s = _row_vec("lse_s", lse_s, rows, dev, lead)
+    if teacher:
+        if kl_rows is None:
+            raise ValueError("teacher gradients need the forward's kl_rows")
+        kl_rows = _row_vec("kl_rows", kl_rows, rows, dev, lead)
+    if grad_rows is not None:
+        grad_rows = _row_vec("grad_rows", grad_rows, rows, dev, lead)
+    dzs = torch.empty((rows, V), dtype=zs.dtype, device=dev)
+    dzt = torch.empty((rows, V), dtype=zs.dtype, device=dev) if teacher else None
+    code = lib.streamkl_vocab_bwd(zt.data_ptr(), zs.data_ptr(), _dtype_code(zt), rows, V, ld_t, ld_s,
+                                  float(temperature), lse_t.data_ptr(), lse_s.data_ptr(),
+                                  kl_rows.data_ptr() if teacher else None,
+                                  grad_rows.data_ptr() if grad_rows is not None else None, float(grad_scalar),
+                                  dzs.data_ptr(), dzt.data_ptr() if dzt is not None else None, _stream_ptr(dev))
+    _check("streamkl_vocab_bwd", code)
+    shape = lead + (V,)
+    return (dzs.view(shape), dzt.view(shape)) if teacher else dzs.view(shape)
+
+
+def streamkl_vocab_fwd_bwd(z_t, z_s, temperature=1.0, grad_rows=None, grad_scalar=1.0, teacher=False,
+                           with_sum=True):
+    """Loss and gradients in one launch for upstream weights known up front:
+    returns (kl_rows, lse_t, lse_s, kl_sum, dz_s, dz_t); dz_t is None unless
+    teacher."""
+    import torch
+    lib = load_library()
+    zt, zs, lead, rows, V, ld_t, ld_s = _vocab_rows(z_t, z_s)
+    dev = zt.device
+    if grad_rows is not None:
+        grad_rows = _row_vec("grad_rows", grad_rows, rows, dev, lead)
+    kl = torch.empty(lead, dtype=torch.float32, device=dev)
+    lt, ls = torch.empty_like(kl), torch.empty_like(kl)
+    tot = torch.empty((1,), dtype=torch.float32, device=dev) if with_sum else None
+    dzs = torch.empty((rows, V), dtype=zs.dtype, device=dev)
+    dzt = torch.empty((rows, V), dtype=zs.dtype, device=dev) if teacher else None
+    code = lib.streamkl_vocab_fwd_bwd(zt.data_ptr(), zs.data_ptr(), _dtype_code(zt), rows, V, ld_t, ld_s,
+                                      float(temperature), grad_rows.data_ptr() if grad_rows is not None else None,
+                                      float(grad_scalar), kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
+                                      tot.data_ptr() if tot is not None else None, dzs.data_ptr(),
+                                      dzt.data_ptr() if dzt is not None else None, _stream_ptr(dev))
+    _check("streamkl_vocab_fwd_bwd", code)
+    shape = lead + (V,)
+    return kl, lt, ls, tot, dzs.view(shape), (dzt.view(shape) if dzt is not None else None)
+
+
 def _autograd_function():
     import torch
 
@@ -293,7 +406,47 @@ def _autograd_function():
     return StreamKLFunction
 
 
+def _vocab_autograd_function():
+    import torch
+
+    class VocabKLFunction(torch.autograd.Function):
+        """Per-row vocabulary KL with gradients for z_s, and for z_t when it
+        requires them.  forward(z_t, z_s, temperature) -> kl_rows [...]"""
+
+        @staticmethod
+        def forward(ctx, z_t, z_s, temperature=1.0):
+            kl, lt, ls, _ = streamkl_vocab_fwd(z_t, z_s, temperature, with_sum=False)
+            ctx.save_for_backward(z_t, z_s, lt, ls, kl)
+            ctx.temperature = temperature
+            return kl
+
+        @staticmethod
+        def backward(ctx, g):
+            z_t, z_s, lt, ls, kl = ctx.saved_tensors
+            g = g.to(torch.float32).contiguous()
+            want_t = ctx.needs_input_grad[0]
+            if not (want_t or ctx.needs_input_grad[1]):
+                return None, None, None
+            out = streamkl_vocab_bwd(z_t, z_s, lt, ls, kl, ctx.temperature, grad_rows=g, teacher=want_t)
+            dzs, dzt = out if want_t else (out, None)
+            return dzt, (dzs if ctx.needs_input_grad[1] else None), None
+
+    return VocabKLFunction
+
+
 _fn_cache = None
+_vocab_fn_cache = None
+
+
+def vocab_kl(z_t, z_s, temperature=1.0):
+    """Differentiable per-row KL(softmax(z_t / T) || softmax(z_s / T)) over the
+    last dimension (shape z_t.shape[:-1]); gradients flow to z_s and, when it
+    requires them, to z_t.  The T^2 factor of the distillation loss is the
+    caller's (multiply the result)."""
+    global _vocab_fn_cache
+    if _vocab_fn_cache is None:
+        _vocab_fn_cache = _vocab_autograd_function()
+    return _vocab_fn_cache.apply(z_t, z_s, temperature)
 
 
 def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
@@ -307,5 +460,5 @@ def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
 
 
 __all__ = ["streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
-           "attention_kl", "load_library", "supported", "status_string",
+           "attention_kl", "streamkl_vocab_fwd", "streamkl_vocab_bwd", "streamkl_vocab_fwd_bwd", "vocab_kl", "load_library", "supported", "status_string",
            "StreamKLError", "STREAMKL_F32", "STREAMKL_BF16"]

@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include "streamkl.h"
+#include "streamkl_internal.h"
 
 namespace {
 
@@ -1337,3 +1338,10 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
 }
 
 }  // extern "C"
+
+namespace streamkl_internal {
+hipError_t launch_row_sum(const float *x, int64_t n, float *out, hipStream_t s) {
+    hipLaunchKernelGGL(streamkl_sum_kernel, dim3(1), dim3(1024), 0, s, x, n, out);
+    return hipGetLastError();
+}
+}  // namespace streamkl_internal

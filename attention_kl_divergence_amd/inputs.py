@@ -77,9 +77,10 @@ WORKLOADS = {
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32 holding bf16 values."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    # finite inputs: the sum stays below 2^32 (largest finite pattern 0xFF7FFFFF)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(x.shape)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -136,3 +137,79 @@ def upstream_grad(B: int, H: int, n_q: int, seed: int) -> np.ndarray:
     """Random per-row upstream gradients dL/dKL_r (float32, N(0, 1))."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.standard_normal((B, H, n_q), dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Vocabulary-logit workloads (distillation loss over output logits).  The pages
+# name no dataset or model for them; the logits are synthetic with the
+# character of language-model outputs: a broad Gaussian body plus a few
+# strongly preferred tokens per row, and a student that is a noisy copy of the
+# teacher.  Each row is drawn from its own generator (seed, row), so any subset
+# of rows can be regenerated on its own.
+#
+# Recipe "lm" (float32, in this order per row): z_t = 2.5 N(0, 1) over V; 16
+# token indices uniform in [0, V) (repeats allowed) each get + U(4, 12); then
+# z_s = z_t + sigma N(0, 1).  "iid": z_t, z_s independent 2.5 N(0, 1).
+# bf16 workloads round both once (ties to even).
+
+@dataclasses.dataclass(frozen=True)
+class VocabWorkload:
+    name: str
+    rows: int
+    V: int
+    dtype: str          # "bf16" or "f32"
+    temperature: float
+    recipe: str         # "lm" | "iid"
+    sigma: float
+    seed: int
+
+    def resized(self, **kw) -> "VocabWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+VOCAB_WORKLOADS = {
+    "kd_logits_small": VocabWorkload("kd_logits_small", 37, 32000, "bf16", 2.0, "lm", 0.5, 31),
+    "kd_logits_odd_f32": VocabWorkload("kd_logits_odd_f32", 9, 50257, "f32", 1.0, "lm", 0.5, 32),
+    "kd_logits_short": VocabWorkload("kd_logits_short", 70, 1000, "bf16", 4.0, "iid", 0.0, 33),
+    "kd_logits_4k_128k": VocabWorkload("kd_logits_4k_128k", 4096, 128256, "bf16", 2.0, "lm", 0.5, 34),
+}
+
+
+def make_vocab(w: VocabWorkload, rows=None, threads: int = 8) -> tuple:
+    """Teacher and student logits of ``w`` as float32 arrays [n, V] exactly
+    representable in ``w.dtype``; ``rows`` (an iterable of row indices) selects
+    a subset, default all rows.  Rows are drawn on ``threads`` threads (each
+    row from its own generator, so the result does not depend on it)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    idx = list(range(w.rows)) if rows is None else [int(r) for r in rows]
+    if w.recipe not in ("lm", "iid"):
+        raise ValueError(f"unknown vocab recipe {w.recipe}")
+    if w.dtype not in ("bf16", "f32"):
+        raise ValueError(f"unknown dtype {w.dtype}")
+    zt = np.empty((len(idx), w.V), dtype=np.float32)
+    zs = np.empty((len(idx), w.V), dtype=np.float32)
+    body = np.float32(2.5)
+
+    def one(n):
+        rng = np.random.Generator(np.random.PCG64([w.seed, idx[n]]))
+        t = zt[n]
+        rng.standard_normal(out=t, dtype=np.float32)
+        t *= body
+        s = zs[n]
+        if w.recipe == "lm":
+            hot = rng.integers(0, w.V, size=16)
+            t[hot] += rng.uniform(4.0, 12.0, size=16).astype(np.float32)
+            rng.standard_normal(out=s, dtype=np.float32)
+            s *= np.float32(w.sigma)
+            s += t
+        else:
+            rng.standard_normal(out=s, dtype=np.float32)
+            s *= body
+        if w.dtype == "bf16":
+            zt[n] = round_bf16(t)
+            zs[n] = round_bf16(s)
+
+    with ThreadPoolExecutor(max_workers=max(1, int(threads))) as ex:
+        list(ex.map(one, range(len(idx))))
+    return zt, zs

@@ -24,6 +24,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        timed in its own loop after the headline steps)
        python bench.py --copy-calibration MiB   (a plain device copy of known
                        size, run under the same HBM byte counters to scale them)
+       python bench.py --vocab [--vocab-workload NAME] [--cpu-rows N]
+                       (the vocabulary-logit KL: forward + student backward per
+                       step, the fused launch timed beside it; HBM roofline)
 """
 import argparse
 import hashlib
@@ -78,12 +81,12 @@ def materialized_baseline_peak(w, d, torch):
         return None
 
 
-def kernel_source_hash():
-    with open(os.path.join(ROOT, "attention_kl_divergence_amd", "csrc", "streamkl.hip"), "rb") as f:
+def kernel_source_hash(src="streamkl.hip"):
+    with open(os.path.join(ROOT, "attention_kl_divergence_amd", "csrc", src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def committed_traffic(kernel, workload):
+def committed_traffic(kernel, workload, src="streamkl.hip"):
     """HBM bytes per launch from the committed counter summary, if the kernel
     source is unchanged since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.txt")
@@ -95,7 +98,7 @@ def committed_traffic(kernel, workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_hash():
+    if vals.get("source_sha256") != kernel_source_hash(src):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -139,6 +142,149 @@ def cpu_baseline(w, x, heads):
                       f"({w.n_q} query rows x {w.n_k} keys each, {(f + b) / 1e9:.1f} GFLOP algorithmic)"}
 
 
+def vocab_bytes(w):
+    """Algorithmic HBM bytes of the vocabulary-KL launches: the forward reads
+    both logit matrices once and writes 3 fp32 per row; the backward reads both
+    matrices and the 2 saved fp32 per row (3 with the teacher gradient) and
+    writes dz_s; the fused launch reads both matrices once (its second pass
+    re-reads rows the first has just read) and writes the row outputs and dz_s."""
+    elt = 2 if w.dtype == "bf16" else 4
+    mat = w.rows * w.V * elt
+    return {"fwd": 2 * mat + 12 * w.rows, "bwd": 3 * mat + 8 * w.rows, "fused": 3 * mat + 12 * w.rows}
+
+
+def vocab_cpu_baseline(w, zt, zs, rows):
+    """The fp64 oracle, as it stands, on the first `rows` rows of the workload
+    (all rows if 0; forward and student backward), fed 512 rows at a time;
+    only the oracle calls are timed."""
+    import numpy as np
+
+    import oracle
+    rows = w.rows if rows <= 0 else max(1, min(rows, w.rows))
+    dt = 0.0
+    for r0 in range(0, rows, 512):
+        a = zt[r0:min(rows, r0 + 512)].astype(np.float64)
+        b = zs[r0:min(rows, r0 + 512)].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.vocab_fwd(a, b, w.temperature)
+        oracle.vocab_bwd(a, b, w.temperature)
+        dt += time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"fp64 oracle forward + student backward of {rows} of the {w.rows} rows "
+                      f"({w.V} logits each)"}
+
+
+def vocab_main(args):
+    """Vocabulary-logit KL: one step = forward (per-row KL, LSEs, sum) +
+    student backward, the launches an autograd loss.backward() makes; the
+    fused forward+backward launch is timed beside it."""
+    import numpy as np
+    import torch
+
+    import attention_kl_divergence_amd as skl
+    from attention_kl_divergence_amd import inputs
+
+    w = inputs.VOCAB_WORKLOADS[args.vocab_workload]
+    print(f"[bench] drawing {w}", file=sys.stderr, flush=True)
+    zt_h, zs_h = inputs.make_vocab(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    zt = torch.from_numpy(zt_h).to(tdt).cuda()
+    zs = torch.from_numpy(zs_h).to(tdt).cuda()
+    dev = zt.device
+    kl = torch.empty((w.rows,), dtype=torch.float32, device=dev)
+    lt, ls = torch.empty_like(kl), torch.empty_like(kl)
+    tot = torch.empty((1,), dtype=torch.float32, device=dev)
+    dzs = torch.empty((w.rows, w.V), dtype=tdt, device=dev)
+    lib = skl.load_library()
+    code = skl.STREAMKL_BF16 if w.dtype == "bf16" else skl.STREAMKL_F32
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    T = w.temperature
+    g = 1.0 / w.rows  # a mean over rows
+
+    def fwd():
+        rc = lib.streamkl_vocab_fwd(zt.data_ptr(), zs.data_ptr(), code, w.rows, w.V, w.V, w.V, T, kl.data_ptr(),
+                                    lt.data_ptr(), ls.data_ptr(), tot.data_ptr(), sp)
+        if rc:
+            raise RuntimeError(skl.status_string(rc))
+
+    def bwd():
+        rc = lib.streamkl_vocab_bwd(zt.data_ptr(), zs.data_ptr(), code, w.rows, w.V, w.V, w.V, T, lt.data_ptr(),
+                                    ls.data_ptr(), None, None, g, dzs.data_ptr(), None, sp)
+        if rc:
+            raise RuntimeError(skl.status_string(rc))
+
+    def fused():
+        rc = lib.streamkl_vocab_fwd_bwd(zt.data_ptr(), zs.data_ptr(), code, w.rows, w.V, w.V, w.V, T, None, g,
+                                        kl.data_ptr(), lt.data_ptr(), ls.data_ptr(), tot.data_ptr(), dzs.data_ptr(),
+                                        None, sp)
+        if rc:
+            raise RuntimeError(skl.status_string(rc))
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+        fused()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in fev:
+        e[0].record(stream)
+        fused()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_f = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_b = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    t_x = np.array([e[0].elapsed_time(e[1]) for e in fev])
+    nb = vocab_bytes(w)
+    gbs = {k: nb[k] / (np.mean(t) * 1e-3) / 1e9 for k, t in (("fwd", t_f), ("bwd", t_b), ("fused", t_x))}
+    print(f"[bench] vocab fwd {np.mean(t_f):.4f} ms ({gbs['fwd']:.0f} GB/s), bwd {np.mean(t_b):.4f} ms "
+          f"({gbs['bwd']:.0f} GB/s), fused {np.mean(t_x):.4f} ms ({gbs['fused']:.0f} GB/s)",
+          file=sys.stderr, flush=True)
+    dominant = "fwd" if np.mean(t_f) >= np.mean(t_b) else "bwd"
+    dom_kernel = f"streamkl_vocab_{dominant}_kernel"
+    value = (nb["fwd"] + nb["bwd"]) * args.steps / wall / 1e9
+    res = {
+        "metric": "fused vocabulary-logit KL fwd+bwd effective HBM GB/s (algorithmic bytes)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "V": w.V, "temperature": T,
+                   "inputs": f"seeded {w.recipe} logits", "parallelism": "single GPU"},
+        "rows_per_s": round(w.rows * args.steps / wall, 1),
+        "fwd_ms": round(float(np.mean(t_f)), 4), "bwd_ms": round(float(np.mean(t_b)), 4),
+        "fused_fwd_bwd_ms": round(float(np.mean(t_x)), 4),
+        "fwd_gbs": round(gbs["fwd"], 1), "bwd_gbs": round(gbs["bwd"], 1), "fused_gbs": round(gbs["fused"], 1),
+        "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": round(gbs[dominant], 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs[dominant] / PEAK_HBM_GBS, 4),
+                     "traffic": committed_traffic(dom_kernel, w.name, "streamkl_vocab.hip"),
+                     "ms_per_launch": round(float(np.mean(t_f if dominant == "fwd" else t_b)), 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample of rows", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = vocab_cpu_baseline(w, zt_h, zs_h, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +299,11 @@ def main():
                     help="key splits of the forward (default: the library's suggestion for the shape)")
     ap.add_argument("--teacher-grads", action="store_true",
                     help="also time the first-argument (teacher) backward, outside the headline step")
+    ap.add_argument("--vocab", action="store_true",
+                    help="measure the vocabulary-logit KL instead (its own JSON line)")
+    ap.add_argument("--vocab-workload", default="kd_logits_4k_128k")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the vocabulary CPU baseline sample (0: all rows)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this primitive is measured on one GPU only; multi-GPU runs are not supported "
@@ -161,6 +312,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.vocab:
+        vocab_main(args)
         return
 
     import numpy as np

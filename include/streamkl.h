@@ -201,6 +201,67 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
                                      const float *grad_rows, float grad_scalar,
                                      void *dq_t, void *dk_t, void *stream);
 
+/*
+ * Vocabulary-logit KL at temperature.  The distillation loss of "Lecture 05 -
+ * Where It All Lands", section 3.1, applied to output logits: for every row r
+ * of the teacher and student logit matrices z_t, z_s ([rows, V]),
+ *
+ *     p = softmax(z_t[r] / T),   q = softmax(z_s[r] / T),
+ *     KL_r = sum_v p[v] (log p[v] - log q[v])   (nats, teacher first),
+ *
+ * in one streaming pass over each row with the same online (reference max,
+ * normaliser, teacher-weighted accumulator) state as the attention forward; no
+ * [rows, V] intermediate is written.  The T^2 factor of section 3.3 (and any
+ * loss weight) is the caller's, through the upstream gradient.
+ *
+ * Conventions of the vocabulary entry points:
+ *  - z_t, z_s: device pointers, dtype as `dtype` (shared), row r of z_t starts
+ *    at z_t + r * ld_t elements (ld_t >= V), likewise z_s with ld_s; the V
+ *    logits of a row are contiguous.  Pointers must be aligned to the element
+ *    size.  16-byte aligned rows (base 16-byte aligned, ld and V multiples of 8)
+ *    take the vectorised path; any other layout a slower element-wise path.
+ *  - Logits must be finite (a vocabulary mask is expressed by a large negative
+ *    finite logit, e.g. -1e4); temperature in [1e-4, 1e6].
+ *  - Per-row outputs kl_rows, lse_t, lse_s (log-normalisers of z / T) and
+ *    grad_rows are contiguous fp32 [rows]; gradients dz_s, dz_t are contiguous
+ *    [rows, V] in the input dtype, overwritten.
+ *  - rows >= 1, 1 <= V <= 2^30 (INVALID otherwise, as for a null pointer, a
+ *    misaligned pointer or a bad temperature).  A row is owned by one wave
+ *    (V < 4096, four rows per workgroup) or one workgroup; launches cover at
+ *    most 2^20 rows each, so any row count is served by consecutive launches.
+ *  - No workspace, no atomics, deterministic; stream and error behaviour as
+ *    for the attention entry points.
+ */
+
+/* Forward: kl_rows, lse_t, lse_s (out, required) and, if kl_sum is not NULL,
+ * their deterministic sum (one fp32 device scalar). */
+streamkl_status streamkl_vocab_fwd(const void *z_t, const void *z_s, streamkl_dtype dtype, int64_t rows, int V,
+                                   int64_t ld_t, int64_t ld_s, float temperature, float *kl_rows, float *lse_t,
+                                   float *lse_s, float *kl_sum, void *stream);
+
+/* Backward of L = sum_r g_r KL_r (g_r = grad_rows[r], or grad_scalar for
+ * every row when grad_rows is NULL), recomputing p and q from the forward's
+ * lse_t, lse_s:
+ *     dz_s[r][v] = g_r / T * (q[v] - p[v])
+ *     dz_t[r][v] = g_r / T * p[v] * ((z_t - z_s)[r][v] / T - LSE_t + LSE_s - KL_r)
+ * dz_s: out, required.  dz_t: out, or NULL for student gradients only; when
+ * given, kl_rows (the forward's) is required. */
+streamkl_status streamkl_vocab_bwd(const void *z_t, const void *z_s, streamkl_dtype dtype, int64_t rows, int V,
+                                   int64_t ld_t, int64_t ld_s, float temperature, const float *lse_t,
+                                   const float *lse_s, const float *kl_rows, const float *grad_rows,
+                                   float grad_scalar, void *dz_s, void *dz_t, void *stream);
+
+/* Forward and backward in one launch, for callers that know the upstream
+ * weights before the loss is computed (a plain sum or mean of the per-row KL,
+ * with or without the T^2 factor): each row is read for the forward and again
+ * for the gradients right after, while its logits are still in the caches.
+ * Outputs as streamkl_vocab_fwd plus dz_s (required) and dz_t (optional) as
+ * streamkl_vocab_bwd. */
+streamkl_status streamkl_vocab_fwd_bwd(const void *z_t, const void *z_s, streamkl_dtype dtype, int64_t rows, int V,
+                                       int64_t ld_t, int64_t ld_s, float temperature, const float *grad_rows,
+                                       float grad_scalar, float *kl_rows, float *lse_t, float *lse_s,
+                                       float *kl_sum, void *dz_s, void *dz_t, void *stream);
+
 /* Bytes of device memory, beyond the caller's inputs and required outputs, that
  * the library needs for a call of this shape: always 0 here (the saved
  * log-normalisers are an output of streamkl_fwd). */

@@ -168,3 +168,48 @@ def test_split_forward_pieces_reject_bad_arguments_before_any_hip_call():
     assert lib.streamkl_fwd_split_count(2, 16, 16384, 16384, 0) == 1
     assert lib.streamkl_fwd_split_count(4, 12, 2048, 2048, 0) == 2
     assert lib.streamkl_fwd_split_count(1, 1, 128, 128, 0) == 1
+
+
+def test_vocab_entry_points_reject_bad_arguments_before_any_hip_call():
+    lib = skl.load_library()
+    BF = skl.STREAMKL_BF16
+    zt, zs, out = A, A + 0x10000000, A + 0x20000000
+
+    def fwd(z_t=zt, z_s=zs, dtype=BF, rows=4, V=1000, ld_t=1000, ld_s=1000, T=2.0, kl=out, lt=out + 64,
+            ls=out + 128):
+        return lib.streamkl_vocab_fwd(z_t, z_s, dtype, rows, V, ld_t, ld_s, T, kl, lt, ls, None, None)
+    assert fwd(z_t=None) == INV and fwd(z_s=None) == INV
+    assert fwd(dtype=7) == INV
+    assert fwd(rows=0) == INV and fwd(V=0) == INV and fwd(V=(1 << 30) + 1, ld_t=1 << 31, ld_s=1 << 31) == INV
+    assert fwd(ld_t=999) == INV and fwd(ld_s=10) == INV
+    assert fwd(T=0.0) == INV and fwd(T=-1.0) == INV and fwd(T=float("nan")) == INV and fwd(T=2e6) == INV
+    assert fwd(T=float("inf")) == INV
+    assert fwd(z_t=zt + 1) == INV                      # not aligned to the bf16 element
+    assert fwd(dtype=skl.STREAMKL_F32, z_s=zs + 2) == INV  # not aligned to the fp32 element
+    assert fwd(kl=None) == INV and fwd(lt=None) == INV and fwd(ls=None) == INV
+    assert fwd(rows=1 << 60, V=8192, ld_t=8192, ld_s=8192) == INV   # row offsets beyond the address space
+
+    def bwd(lt=out, ls=out + 64, kl=None, g=None, dzs=out + 0x1000, dzt=None, **kw):
+        a = dict(z_t=zt, z_s=zs, dtype=BF, rows=4, V=1000, ld_t=1000, ld_s=1000, T=2.0); a.update(kw)
+        return lib.streamkl_vocab_bwd(a["z_t"], a["z_s"], a["dtype"], a["rows"], a["V"], a["ld_t"], a["ld_s"],
+                                      a["T"], lt, ls, kl, g, 1.0, dzs, dzt, None)
+    assert bwd(lt=None) == INV and bwd(ls=None) == INV
+    assert bwd(dzs=None) == INV and bwd(dzs=out + 0x1001) == INV
+    assert bwd(dzt=out + 0x2000) == INV                # teacher gradients need kl_rows
+    assert bwd(dzt=out + 0x2001, kl=out + 128) == INV  # misaligned dz_t
+    assert bwd(T=0.0) == INV and bwd(rows=0) == INV
+
+    def fused(kl=out, dzs=out + 0x1000, **kw):
+        a = dict(z_t=zt, z_s=zs, dtype=BF, rows=4, V=1000, ld_t=1000, ld_s=1000, T=2.0); a.update(kw)
+        return lib.streamkl_vocab_fwd_bwd(a["z_t"], a["z_s"], a["dtype"], a["rows"], a["V"], a["ld_t"], a["ld_s"],
+                                          a["T"], None, 1.0, kl, out + 64, out + 128, None, dzs, None, None)
+    assert fused(kl=None) == INV and fused(dzs=None) == INV and fused(V=0) == INV and fused(ld_s=5) == INV
+
+
+def test_vocab_binding_fails_loudly_without_device_tensors():
+    import torch
+    z = torch.zeros(2, 16)
+    with pytest.raises(ValueError):
+        skl.streamkl_vocab_fwd(z, z)
+    with pytest.raises(ValueError):
+        skl.vocab_kl(z, z)

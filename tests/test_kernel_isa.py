@@ -83,3 +83,30 @@ def test_no_spills_in_the_mfma_loops(asm):
                 mfma += 1
             elif "scratch_" in line:
                 scratch += 1
+
+
+def test_vocab_kernels_do_not_spill_and_stay_vectorised(tmp_path):
+    """The vocabulary-logit kernels stream HBM: no register spills (private
+    segment 0) in any instantiation, and the vector paths move the logits with
+    16-byte loads."""
+    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path / "vocab.s"
+    flags = [f for f in hip_build.FLAGS if f not in ("-shared",)]
+    res = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), hip_build.SRCS[1]],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = out.read_text()
+    found = re.findall(r"\.name:\s+(_ZN12_GLOBAL__N_1\d+streamkl_vocab_\w+)[\s\S]*?"
+                       r"\.private_segment_fixed_size:\s+(\d+)", text)
+    # {bf16, f32} x {vector, element} x (forward {1,4,8,16} waves per row + backward and fused
+    # {student, teacher} x {1,4,8,16})
+    assert len(found) == 2 * 2 * (4 + 2 * 2 * 4)
+    for name, priv in found:
+        assert int(priv) == 0, name
+    lines = text.split("\n")
+    starts = [i for i, l in enumerate(lines) if re.match(r"^_ZN12_GLOBAL__N_1\d+streamkl_vocab_fwd_kernelIDF16bLb1E", l)]
+    assert starts
+    for i in starts:
+        end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
+        assert any("global_load_dwordx4" in l for l in lines[i:end])
