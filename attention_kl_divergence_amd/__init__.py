@@ -29,6 +29,13 @@ STREAMKL_F32, STREAMKL_BF16 = 0, 1
 _lib = None
 
 
+class StreamKLLayout(ctypes.Structure):
+    """streamkl_layout: head counts of q_t, k_t, q_s, k_s (0 = H) and per-batch
+    valid lengths (device int32 [B] pointers, or None)."""
+    _fields_ = [("heads_q_t", ctypes.c_int), ("heads_k_t", ctypes.c_int), ("heads_q_s", ctypes.c_int),
+                ("heads_k_s", ctypes.c_int), ("seqlen_q", ctypes.c_void_p), ("seqlen_k", ctypes.c_void_p)]
+
+
 class StreamKLError(RuntimeError):
     def __init__(self, where: str, code: int, text: str):
         super().__init__(f"{where} failed: status {code} ({text})")
@@ -64,6 +71,15 @@ def load_library():
     lib.streamkl_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, i, vp, sz, vp, vp, vp,
                                        vp, vp]
     lib.streamkl_fwd_split.restype = i
+    lay = ctypes.POINTER(StreamKLLayout)
+    lib.streamkl_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, lay, f, f, i, vp, vp, vp, vp, vp]
+    lib.streamkl_fwd_ex.restype = i
+    lib.streamkl_bwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, lay, f, f, i, vp, vp, vp, f, vp, vp,
+                                    vp]
+    lib.streamkl_bwd_ex.restype = i
+    lib.streamkl_bwd_teacher_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, lay, f, f, i, vp, vp, vp, vp,
+                                            f, vp, vp, vp]
+    lib.streamkl_bwd_teacher_ex.restype = i
     i64 = ctypes.c_int64
     lib.streamkl_vocab_fwd.argtypes = [vp, vp, i, i64, i, i64, i64, f, vp, vp, vp, vp, vp]
     lib.streamkl_vocab_fwd.restype = i
@@ -104,25 +120,57 @@ def _dtype_code(t):
 
 
 def _inputs(q_t, k_t, q_s, k_s):
+    """Check the four [B, heads, N, d] tensors; returns ((B, H, n_q, n_k, d_t,
+    d_s), strides, heads) with H the number of KL heads (the larger query head
+    count) and heads the four tensors' own head counts."""
     import torch
     ts = (q_t, k_t, q_s, k_s)
     for t in ts:
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
-            raise ValueError("q_t, k_t, q_s, k_s must be 4-D tensors [B, H, N, d]")
+            raise ValueError("q_t, k_t, q_s, k_s must be 4-D tensors [B, heads, N, d]")
         if t.device.type != "cuda":
             raise ValueError("inputs must be device (HIP) tensors")
         if t.stride(-1) != 1:
             raise ValueError("the last dimension must be contiguous")
     if len({t.dtype for t in ts}) != 1 or len({t.device for t in ts}) != 1:
         raise ValueError("inputs must share dtype and device")
-    B, H, n_q, d_t = q_t.shape
-    n_k = k_t.shape[2]
-    d_s = q_s.shape[3]
-    if tuple(k_t.shape) != (B, H, n_k, d_t) or tuple(q_s.shape) != (B, H, n_q, d_s) or \
-            tuple(k_s.shape) != (B, H, n_k, d_s):
-        raise ValueError("inconsistent shapes: q_t [B,H,Nq,dt], k_t [B,H,Nk,dt], q_s [B,H,Nq,ds], k_s [B,H,Nk,ds]")
+    B, hq_t, n_q, d_t = q_t.shape
+    hk_t, n_k = k_t.shape[1], k_t.shape[2]
+    hq_s, d_s = q_s.shape[1], q_s.shape[3]
+    hk_s = k_s.shape[1]
+    if tuple(k_t.shape) != (B, hk_t, n_k, d_t) or tuple(q_s.shape) != (B, hq_s, n_q, d_s) or \
+            tuple(k_s.shape) != (B, hk_s, n_k, d_s):
+        raise ValueError("inconsistent shapes: q_t [B,Hqt,Nq,dt], k_t [B,Hkt,Nk,dt], q_s [B,Hqs,Nq,ds], "
+                         "k_s [B,Hks,Nk,ds]")
+    H = max(hq_t, hq_s)
+    if H % hq_t or H % hq_s or hq_t % hk_t or hq_s % hk_s:
+        raise ValueError("head counts must nest: each query head count divides the larger one and each key "
+                         "head count divides its model's query head count")
     strides = (ctypes.c_int64 * 12)(*[s for t in ts for s in (t.stride(0), t.stride(1), t.stride(2))])
-    return (B, H, n_q, n_k, d_t, d_s), strides
+    return (B, H, n_q, n_k, d_t, d_s), strides, (hq_t, hk_t, hq_s, hk_s)
+
+
+def _layout(B, H, heads, seqlen_q, seqlen_k, dev):
+    """A StreamKLLayout when head counts differ or lengths are given, else None.
+    Also returns the int32 length tensors it points to (kept alive by the caller)."""
+    import torch
+    if all(h == H for h in heads) and seqlen_q is None and seqlen_k is None:
+        return None, ()
+    keep = []
+    ptrs = []
+    for name, t in (("seqlen_q", seqlen_q), ("seqlen_k", seqlen_k)):
+        if t is None:
+            ptrs.append(None)
+            continue
+        if not isinstance(t, torch.Tensor):
+            t = torch.tensor(t, dtype=torch.int32, device=dev)
+        if t.dtype != torch.int32 or t.device != dev or tuple(t.shape) != (B,):
+            raise ValueError(f"{name} must be an int32 [B] tensor on the inputs' device")
+        t = t.contiguous()
+        keep.append(t)
+        ptrs.append(t.data_ptr())
+    lay = StreamKLLayout(heads[0], heads[1], heads[2], heads[3], ptrs[0], ptrs[1])
+    return lay, tuple(keep)
 
 
 def _stream_ptr(device):
@@ -135,23 +183,38 @@ def _taus(tau_t, tau_s, d_t, d_s):
             float(1.0 / math.sqrt(d_s)) if tau_s is None else float(tau_s))
 
 
-def streamkl_fwd(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, with_sum=True, split=None):
+def streamkl_fwd(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, with_sum=True, split=None,
+                 seqlen_q=None, seqlen_k=None):
     """Forward: returns (kl_rows, lse_t, lse_s, kl_sum), fp32 device tensors.
 
     kl_rows/lse_t/lse_s are [B, H, N_Q]; kl_sum is a 1-element tensor (None if
     with_sum is False).  tau defaults to 1/sqrt(d) per side.  split: number of
     key ranges run as separate workgroups and merged (split-K); None takes the
     library's suggestion for the shape (1 when the GPU is already full).
+
+    Grouped heads: the four tensors may have their own head counts (see
+    include/streamkl.h): H is the larger query head count, a model with fewer
+    query heads is broadcast over consecutive KL heads and keys are shared by
+    consecutive query heads.  seqlen_q / seqlen_k: int32 [B] valid lengths of
+    each batch inside the padded N_Q / N_K (rows past them are empty: KL 0).
     """
     import torch
     lib = load_library()
-    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs(q_t, k_t, q_s, k_s)
     tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
     dev = q_t.device
     kl = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
     lt = torch.empty_like(kl)
     ls = torch.empty_like(kl)
     tot = torch.empty((1,), dtype=torch.float32, device=dev) if with_sum else None
+    lay, _keep = _layout(B, H, heads, seqlen_q, seqlen_k, dev)
+    if lay is not None:
+        code = lib.streamkl_fwd_ex(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
+                                   B, H, n_q, n_k, d_t, d_s, strides, ctypes.byref(lay), tau_t, tau_s,
+                                   int(bool(causal)), kl.data_ptr(), lt.data_ptr(), ls.data_ptr(),
+                                   tot.data_ptr() if tot is not None else None, _stream_ptr(dev))
+        _check("streamkl_fwd_ex", code)
+        return kl, lt, ls, tot
     n_split = int(lib.streamkl_fwd_split_count(B, H, n_q, n_k, int(bool(causal)))) if split is None else int(split)
     if n_split > 1:
         nbytes = int(lib.streamkl_fwd_split_workspace_size(B, H, n_q, n_split))
@@ -180,7 +243,9 @@ def streamkl_fwd_partial(q_t, k_t, q_s, k_s, k_begin, k_end, tau_t=None, tau_s=N
     states of disjoint key ranges combine with streamkl_fwd_merge."""
     import torch
     lib = load_library()
-    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs(q_t, k_t, q_s, k_s)
+    if any(h != H for h in heads):
+        raise ValueError("streamkl_fwd_partial takes equal head counts")
     tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
     dev = q_t.device
     st = torch.empty((B, H, n_q, STATE_FLOATS), dtype=torch.float32, device=dev)
@@ -214,22 +279,32 @@ def streamkl_fwd_merge(states, tau_t, tau_s, with_sum=True):
 
 
 def streamkl_bwd(q_t, k_t, q_s, k_s, lse_t, lse_s, grad_rows=None, grad_scalar=1.0,
-                 tau_t=None, tau_s=None, causal=False):
-    """Backward: returns (dq_s, dk_s) in the input dtype for L = sum_r g_r KL_r.
+                 tau_t=None, tau_s=None, causal=False, seqlen_q=None, seqlen_k=None):
+    """Backward: returns (dq_s, dk_s) in the input dtype for L = sum_r g_r KL_r,
+    shaped like q_s and k_s (a head shared by several KL heads gets the sum).
 
     grad_rows: fp32 [B, H, N_Q] device tensor of dL/dKL_r, or None to use
-    grad_scalar for every row.
+    grad_scalar for every row.  seqlen_q / seqlen_k as in streamkl_fwd.
     """
     import torch
     lib = load_library()
-    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs(q_t, k_t, q_s, k_s)
     tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
     dev = q_t.device
     for name, t in (("lse_t", lse_t), ("lse_s", lse_s)) + ((("grad_rows", grad_rows),) if grad_rows is not None else ()):
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, n_q) or t.device != dev:
             raise ValueError(f"{name} must be a contiguous fp32 [B, H, N_Q] tensor on the inputs' device")
-    dq = torch.empty((B, H, n_q, d_s), dtype=q_s.dtype, device=dev)
-    dk = torch.empty((B, H, n_k, d_s), dtype=q_s.dtype, device=dev)
+    dq = torch.empty((B, heads[2], n_q, d_s), dtype=q_s.dtype, device=dev)
+    dk = torch.empty((B, heads[3], n_k, d_s), dtype=q_s.dtype, device=dev)
+    lay, _keep = _layout(B, H, heads, seqlen_q, seqlen_k, dev)
+    if lay is not None:
+        code = lib.streamkl_bwd_ex(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
+                                   B, H, n_q, n_k, d_t, d_s, strides, ctypes.byref(lay), tau_t, tau_s,
+                                   int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr(),
+                                   grad_rows.data_ptr() if grad_rows is not None else None, float(grad_scalar),
+                                   dq.data_ptr(), dk.data_ptr(), _stream_ptr(dev))
+        _check("streamkl_bwd_ex", code)
+        return dq, dk
     code = lib.streamkl_bwd(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
                             B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, int(bool(causal)),
                             lse_t.data_ptr(), lse_s.data_ptr(),
@@ -240,14 +315,15 @@ def streamkl_bwd(q_t, k_t, q_s, k_s, lse_t, lse_s, grad_rows=None, grad_scalar=1
 
 
 def streamkl_bwd_teacher(q_t, k_t, q_s, k_s, lse_t, lse_s, kl_rows, grad_rows=None, grad_scalar=1.0,
-                         tau_t=None, tau_s=None, causal=False):
+                         tau_t=None, tau_s=None, causal=False, seqlen_q=None, seqlen_k=None):
     """Backward with respect to the first (teacher) distribution: returns
-    (dq_t, dk_t) in the input dtype for L = sum_r g_r KL_r.  kl_rows, lse_t and
-    lse_s are the forward's outputs.  With the two distributions swapped it
-    gives the student gradients of the reverse divergence KL(P_s || P_t)."""
+    (dq_t, dk_t) in the input dtype for L = sum_r g_r KL_r, shaped like q_t and
+    k_t.  kl_rows, lse_t and lse_s are the forward's outputs.  With the two
+    distributions swapped it gives the student gradients of the reverse
+    divergence KL(P_s || P_t)."""
     import torch
     lib = load_library()
-    (B, H, n_q, n_k, d_t, d_s), strides = _inputs(q_t, k_t, q_s, k_s)
+    (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs(q_t, k_t, q_s, k_s)
     tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
     dev = q_t.device
     rowargs = (("lse_t", lse_t), ("lse_s", lse_s), ("kl_rows", kl_rows)) + \
@@ -255,8 +331,18 @@ def streamkl_bwd_teacher(q_t, k_t, q_s, k_s, lse_t, lse_s, kl_rows, grad_rows=No
     for name, t in rowargs:
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, n_q) or t.device != dev:
             raise ValueError(f"{name} must be a contiguous fp32 [B, H, N_Q] tensor on the inputs' device")
-    dq = torch.empty((B, H, n_q, d_t), dtype=q_t.dtype, device=dev)
-    dk = torch.empty((B, H, n_k, d_t), dtype=q_t.dtype, device=dev)
+    dq = torch.empty((B, heads[0], n_q, d_t), dtype=q_t.dtype, device=dev)
+    dk = torch.empty((B, heads[1], n_k, d_t), dtype=q_t.dtype, device=dev)
+    lay, _keep = _layout(B, H, heads, seqlen_q, seqlen_k, dev)
+    if lay is not None:
+        code = lib.streamkl_bwd_teacher_ex(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),
+                                           _dtype_code(q_t), B, H, n_q, n_k, d_t, d_s, strides, ctypes.byref(lay),
+                                           tau_t, tau_s, int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr(),
+                                           kl_rows.data_ptr(),
+                                           grad_rows.data_ptr() if grad_rows is not None else None,
+                                           float(grad_scalar), dq.data_ptr(), dk.data_ptr(), _stream_ptr(dev))
+        _check("streamkl_bwd_teacher_ex", code)
+        return dq, dk
     code = lib.streamkl_bwd_teacher(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),
                                     _dtype_code(q_t), B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s,
                                     int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr(), kl_rows.data_ptr(),
@@ -383,25 +469,26 @@ def _autograd_function():
         """
 
         @staticmethod
-        def forward(ctx, q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
-            kl, lt, ls, _ = streamkl_fwd(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, with_sum=False)
+        def forward(ctx, q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, seqlen_q=None, seqlen_k=None):
+            kl, lt, ls, _ = streamkl_fwd(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, with_sum=False,
+                                         seqlen_q=seqlen_q, seqlen_k=seqlen_k)
             ctx.save_for_backward(q_t, k_t, q_s, k_s, lt, ls, kl)
-            ctx.cfg = (tau_t, tau_s, causal)
+            ctx.cfg = (tau_t, tau_s, causal, seqlen_q, seqlen_k)
             return kl
 
         @staticmethod
         def backward(ctx, g):
             q_t, k_t, q_s, k_s, lt, ls, kl = ctx.saved_tensors
-            tau_t, tau_s, causal = ctx.cfg
+            tau_t, tau_s, causal, sq, sk = ctx.cfg
             g = g.to(torch.float32).contiguous()
             dq_s = dk_s = dq_t = dk_t = None
             if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
                 dq_s, dk_s = streamkl_bwd(q_t, k_t, q_s, k_s, lt, ls, grad_rows=g,
-                                          tau_t=tau_t, tau_s=tau_s, causal=causal)
+                                          tau_t=tau_t, tau_s=tau_s, causal=causal, seqlen_q=sq, seqlen_k=sk)
             if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
                 dq_t, dk_t = streamkl_bwd_teacher(q_t, k_t, q_s, k_s, lt, ls, kl, grad_rows=g,
-                                                  tau_t=tau_t, tau_s=tau_s, causal=causal)
-            return dq_t, dk_t, dq_s, dk_s, None, None, None
+                                                  tau_t=tau_t, tau_s=tau_s, causal=causal, seqlen_q=sq, seqlen_k=sk)
+            return dq_t, dk_t, dq_s, dk_s, None, None, None, None, None
 
     return StreamKLFunction
 
@@ -449,14 +536,15 @@ def vocab_kl(z_t, z_s, temperature=1.0):
     return _vocab_fn_cache.apply(z_t, z_s, temperature)
 
 
-def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False):
+def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, seqlen_q=None, seqlen_k=None):
     """Differentiable per-row attention KL(P_t || P_s) [B, H, N_Q]; gradients
     flow to whichever of q_s, k_s, q_t, k_t require them.  The reverse
-    divergence KL(P_s || P_t) is attention_kl(q_s, k_s, q_t, k_t, tau_s, tau_t)."""
+    divergence KL(P_s || P_t) is attention_kl(q_s, k_s, q_t, k_t, tau_s, tau_t).
+    Grouped heads and per-batch lengths as in streamkl_fwd."""
     global _fn_cache
     if _fn_cache is None:
         _fn_cache = _autograd_function()
-    return _fn_cache.apply(q_t, k_t, q_s, k_s, tau_t, tau_s, causal)
+    return _fn_cache.apply(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, seqlen_q, seqlen_k)
 
 
 __all__ = ["streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",

@@ -231,7 +231,19 @@ struct FwdParams {
     // online state there ([n_split][rows][6]) instead of the finished row.
     int n_split, k_begin, k_end, k_chunk;
     float *state;
+    // head mapping: KL head h reads head h / g of each tensor (q_t, k_t, q_s,
+    // k_s); per-batch valid lengths (null: n_q, n_k)
+    int g_qt, g_kt, g_qs, g_ks;
+    const int *len_q, *len_k;
 };
+
+// Valid length of batch b from a per-batch array (null: the full length),
+// clamped to [0, n].
+__device__ inline int batch_len(const int *len, int b, int n) {
+    if (!len) return n;
+    const int v = len[b];
+    return v < 0 ? 0 : (v > n ? n : v);
+}
 
 // Scheduler group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
@@ -353,12 +365,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     const int split = rank % p.n_split;
     const int qb = p.n_qblk - 1 - rank / p.n_split;  // high query blocks see the most keys under a causal mask
     const int hh = bh % p.H, bb = bh / p.H;
-    const T *Qt = static_cast<const T *>(p.q_t) + bb * p.st[0] + hh * p.st[1];
-    const T *Kt = static_cast<const T *>(p.k_t) + bb * p.st[3] + hh * p.st[4];
-    const T *Qs = static_cast<const T *>(p.q_s) + bb * p.st[6] + hh * p.st[7];
-    const T *Ks = static_cast<const T *>(p.k_s) + bb * p.st[9] + hh * p.st[10];
+    const T *Qt = static_cast<const T *>(p.q_t) + bb * p.st[0] + (hh / p.g_qt) * p.st[1];
+    const T *Kt = static_cast<const T *>(p.k_t) + bb * p.st[3] + (hh / p.g_kt) * p.st[4];
+    const T *Qs = static_cast<const T *>(p.q_s) + bb * p.st[6] + (hh / p.g_qs) * p.st[7];
+    const T *Ks = static_cast<const T *>(p.k_s) + bb * p.st[9] + (hh / p.g_ks) * p.st[10];
     const int64_t sqt = p.st[2], skt = p.st[5], sqs = p.st[8], sks = p.st[11];
-    const int n_q = p.n_q, n_k = p.n_k, off = n_k - n_q;
+    // valid rows of this batch; the per-row outputs keep the full n_q stride
+    const int n_q = batch_len(p.len_q, bb, p.n_q), n_k = batch_len(p.len_k, bb, p.n_k), off = n_k - n_q;
 
     const int q0w = qb * kBlockX + w * kTile;  // first query of this wave
     const int q = q0w + l32;                   // this lane's query
@@ -451,24 +464,27 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     const float mS = fmaxf(o.ms, ms2);
     const float v1 = fast_exp2(cs * (o.ms - mS)), v2 = fast_exp2(cs * (ms2 - mS));
     const float LS = o.ls * v1 + ls2 * v2;
-    if (hf == 0 && qv) {
-        const int64_t row = ((int64_t)bb * p.H + hh) * n_q + q;
+    if (hf == 0 && q < p.n_q) {
+        // rows past the batch's valid length, and rows with no allowed key,
+        // are empty: KL 0, LSEs 0 (an empty state, L = 0, for partial states)
+        const bool empty = !qv || L == 0.f;
+        const int64_t row = ((int64_t)bb * p.H + hh) * p.n_q + q;
         if (p.state) {
             float *o6 = p.state + ((int64_t)split * p.nheads * n_q + row) * kStateFloats;
-            o6[0] = m;
-            o6[1] = L;
-            o6[2] = AT;
-            o6[3] = AS;
-            o6[4] = mS;
-            o6[5] = LS;
+            o6[0] = empty ? kMasked : m;
+            o6[1] = empty ? 0.f : L;
+            o6[2] = empty ? 0.f : AT;
+            o6[3] = empty ? 0.f : AS;
+            o6[4] = empty ? kMasked : mS;
+            o6[5] = empty ? 0.f : LS;
         } else {
             const float lse_t = p.tau_t * m + logf(L);
             const float lse_s = p.tau_s * mS + logf(LS);
             // E_{P_t}[s_t - s_s] - LSE_t + LSE_s
             const float kl = (p.tau_t * AT - p.tau_s * AS) / L - lse_t + lse_s;
-            p.kl[row] = kl;
-            p.lse_t[row] = lse_t;
-            p.lse_s[row] = lse_s;
+            p.kl[row] = empty ? 0.f : kl;
+            p.lse_t[row] = empty ? 0.f : lse_t;
+            p.lse_s[row] = empty ? 0.f : lse_s;
         }
     }
 }
@@ -501,9 +517,10 @@ __global__ __launch_bounds__(256) void streamkl_merge_kernel(const float *st, in
     }
     const float lt = tau_t * m + logf(L);
     const float ls = tau_s * mS + logf(LS);
-    kl_rows[row] = (tau_t * AT - tau_s * AS) / L - lt + ls;
-    lse_t[row] = lt;
-    lse_s[row] = ls;
+    const bool empty = L == 0.f;  // no allowed key in any state: an empty row
+    kl_rows[row] = empty ? 0.f : (tau_t * AT - tau_s * AS) / L - lt + ls;
+    lse_t[row] = empty ? 0.f : lt;
+    lse_s[row] = empty ? 0.f : ls;
 }
 
 // Deterministic sum of n fp32 values, one block: each thread accumulates a
@@ -545,6 +562,10 @@ struct BwdParams {
     const float *kl;  // per-row KL (first-argument gradients only)
     float g_scalar;
     void *out;
+    // head mapping: KL head h reads head h / g of x_t, x_s, y_t, y_s; the
+    // output has Hout heads, output head o sums KL heads [o group, (o + 1) group)
+    int g_xt, g_xs, g_yt, g_ys, Hout, group;
+    const int *len_q, *len_k;  // per-batch valid lengths (null: n_q, n_k)
 };
 
 // Range [ystart, yend) of streamed rows that stationary block xb meets: all of
@@ -552,19 +573,20 @@ struct BwdParams {
 // the keys up to the block's last query (dq_s), the queries from the block's
 // first key on, rounded down to a tile (dk_s).
 template <bool CAUSAL, bool DKMODE>
-__device__ inline void bwd_range(const BwdParams &p, int xb, int &ystart, int &yend) {
-    const int off = p.n_k - p.n_q;
+__device__ inline void bwd_range(int n_q, int n_k, int n_y, int xb, int &ystart, int &yend) {
+    const int off = n_k - n_q;
     ystart = 0;
-    yend = p.n_y;
+    yend = n_y;
     if (CAUSAL) {
-        if (!DKMODE) yend = min(p.n_k, min(p.n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
+        if (!DKMODE) yend = min(n_k, min(n_q - 1, xb * kBlockX + kBlockX - 1) + off + 1);
         else ystart = (max(0, xb * kBlockX - off) / kBN) * kBN;
     }
 }
+// Streamed tiles of block xb at the full lengths (the work-order estimate).
 template <bool CAUSAL, bool DKMODE>
 __device__ inline int bwd_tiles(const BwdParams &p, int xb) {
     int ys, ye;
-    bwd_range<CAUSAL, DKMODE>(p, xb, ys, ye);
+    bwd_range<CAUSAL, DKMODE>(p.n_q, p.n_k, p.n_y, xb, ys, ye);
     return (ye - ys + kBN - 1) / kBN;
 }
 
@@ -729,7 +751,7 @@ constexpr int kBwdRows = kBwdSub * kBN;
 // each other's MFMA and VALU phases.  GS: the upstream gradient is one scalar.
 // FIRST: gradients with respect to the first (teacher) distribution, contracted
 // with the teacher tiles (output width d_t) instead of the student ones.
-template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE, bool GS, bool FIRST>
+template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE, bool GS, bool FIRST, bool GRP>
 __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams &p, int xb, int bh, char *smem,
                                                                 float (*rowv)[3][kBwdRows]) {
     using TileT = Tile<T, DT>;
@@ -745,24 +767,31 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 
     const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hh = bh % p.H, bb = bh / p.H;
-    const T *Xt = static_cast<const T *>(p.x_t) + bb * p.st[0] + hh * p.st[1];
-    const T *Xs = static_cast<const T *>(p.x_s) + bb * p.st[3] + hh * p.st[4];
-    const T *Yt = static_cast<const T *>(p.y_t) + bb * p.st[6] + hh * p.st[7];
-    const T *Ys = static_cast<const T *>(p.y_s) + bb * p.st[9] + hh * p.st[10];
+    // output head `bh` (of B Hout): batch bb, head ho, fed by KL heads ho group + u
+    const int ho = bh % p.Hout, bb = bh / p.Hout;
+    const T *Xt, *Xs, *Yt, *Ys;  // the current KL head's tensors
+    int64_t rowbase;              // per-query arrays of the current KL head
+    auto set_head = [&](int hh) {
+        Xt = static_cast<const T *>(p.x_t) + bb * p.st[0] + (hh / p.g_xt) * p.st[1];
+        Xs = static_cast<const T *>(p.x_s) + bb * p.st[3] + (hh / p.g_xs) * p.st[4];
+        Yt = static_cast<const T *>(p.y_t) + bb * p.st[6] + (hh / p.g_yt) * p.st[7];
+        Ys = static_cast<const T *>(p.y_s) + bb * p.st[9] + (hh / p.g_ys) * p.st[10];
+        rowbase = ((int64_t)bb * p.H + hh) * p.n_q;
+    };
     const int64_t sxt = p.st[2], sxs = p.st[5], syt = p.st[8], sys = p.st[11];
-    const int n_x = p.n_x, n_y = p.n_y, n_q = p.n_q, off = p.n_k - p.n_q;
-    const int64_t rowbase = ((int64_t)bb * p.H + hh) * n_q;  // per-query arrays of this head
+    // valid lengths of this batch (the arrays keep the full n_q / n_x strides)
+    const int n_qb = batch_len(p.len_q, bb, p.n_q), n_kb = batch_len(p.len_k, bb, p.n_k);
+    const int n_x = DKMODE ? n_kb : n_qb, n_y = DKMODE ? n_qb : n_kb, n_q = n_qb, off = n_kb - n_qb;
 
     const int x0w = xb * kBlockX + w * kTile;
     const int x = x0w + l32;
     const bool xv = x < n_x;
-    const int xc = xv ? x : n_x - 1;
+    const int xc = xv ? x : max(n_x - 1, 0);
     const bool wave_live = x0w < n_x;
 
     int ystart, yend;
-    bwd_range<CAUSAL, DKMODE>(p, xb, ystart, yend);
-    const int ntile = (yend - ystart + kBN - 1) / kBN;
+    bwd_range<CAUSAL, DKMODE>(n_qb, n_kb, n_y, xb, ystart, yend);
+    const int ntile = n_y > 0 ? max(0, (yend - ystart + kBN - 1) / kBN) : 0;
     auto active = [&](int t) {
         const int y0 = ystart + t * kBN;
         if (!wave_live) return false;
@@ -818,31 +847,40 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         }
     };
 
-    issue(0, 0);
-    load_rows(0);
-
-    u32x4 xtv[span_vecs<T, DT>()], xsv[span_vecs<T, DS>()];
-    load_span_global<T, DT>(Xt + (int64_t)xc * sxt, hf, xv, xtv);
-    load_span_global<T, DS>(Xs + (int64_t)xc * sxs, hf, xv, xsv);
-
     const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
+    u32x4 xtv[span_vecs<T, DT>()], xsv[span_vecs<T, DS>()];
     float nlt = 0.f, nls = 0.f, gts = 0.f;  // per-lane row values (dq mode)
     float gsign = w_all < 0.f ? -1.f : 1.f;  // sign(w) applied to the finished gradient when folded
-    if (!DKMODE && xv) {
-        const float wq = ((GS || !p.g) ? p.g_scalar : p.g[rowbase + x]) * tau_g;
-        const float lw = log2f(fabsf(wq));
-        nlt = -p.lse_t[rowbase + x] * kLog2e + lw;
-        if (FIRST) nls = -(p.lse_t[rowbase + x] - p.lse_s[rowbase + x] + p.kl[rowbase + x]);
-        else nls = -p.lse_s[rowbase + x] * kLog2e + lw;
-        gsign = wq < 0.f ? -1.f : 1.f;
-    }
-
     f32x16 G[DG / kTile];
 #pragma unroll
     for (int t = 0; t < DG / kTile; ++t) G[t] = f32x16{};
 
-    store_rows(0);
-    dma_barrier();
+    // Start KL head hh: the first stage's loads, the stationary rows and the
+    // per-lane row values.  G accumulates over the output head's KL heads;
+    // when folded it holds the sum divided by the current head's sign, so a
+    // change of sign between heads negates it.
+    auto begin_head = [&](int hh, bool first_head) {
+        set_head(hh);
+        issue(0, 0);
+        load_rows(0);
+        load_span_global<T, DT>(Xt + (int64_t)xc * sxt, hf, xv, xtv);
+        load_span_global<T, DS>(Xs + (int64_t)xc * sxs, hf, xv, xsv);
+        if (!DKMODE && xv) {
+            const float wq = ((GS || !p.g) ? p.g_scalar : p.g[rowbase + x]) * tau_g;
+            const float lw = log2f(fabsf(wq));
+            nlt = -p.lse_t[rowbase + x] * kLog2e + lw;
+            if (FIRST) nls = -(p.lse_t[rowbase + x] - p.lse_s[rowbase + x] + p.kl[rowbase + x]);
+            else nls = -p.lse_s[rowbase + x] * kLog2e + lw;
+            const float sg = wq < 0.f ? -1.f : 1.f;
+            if (!first_head && sg != gsign) {
+#pragma unroll
+                for (int t = 0; t < DG / kTile; ++t) G[t] = -G[t];
+            }
+            gsign = sg;
+        }
+        store_rows(0);
+        dma_barrier();
+    };
 
     auto ds_grad = [&](const f32x16 &cur_t, const f32x16 &cur_s, int it, int stage, int sub, bool m_cur,
                        auto early_tag) {
@@ -925,26 +963,36 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     }
     const int s_lo = min(nstage, (t_lo + kBwdSub - 1) / kBwdSub);
     const int s_hi = max(s_lo, min(nstage, t_hi / kBwdSub));
-    for (int st = 0; st < s_lo; ++st) stage_body(st, std::false_type{}, st & 1);
-    {
-        // plain stages two at a time, so that the ring slot, and with it every
-        // LDS address, is a compile-time offset
-        int st = s_lo;
-        if (st < s_hi && (st & 1)) stage_body(st++, std::true_type{}, 1);
-        for (; st + 1 < s_hi; st += 2) {
-            stage_body(st, std::true_type{}, 0);
-            stage_body(st + 1, std::true_type{}, 1);
+    // GRP: several KL heads feed this output head (a separate instantiation,
+    // so that the single-head kernels keep their register allocation)
+    const int ngroup = GRP ? p.group : 1;
+    for (int u = 0; u < ngroup; ++u) {
+        begin_head(ho * ngroup + u, u == 0);
+        for (int st = 0; st < s_lo; ++st) stage_body(st, std::false_type{}, st & 1);
+        {
+            // plain stages two at a time, so that the ring slot, and with it
+            // every LDS address, is a compile-time offset
+            int st = s_lo;
+            if (st < s_hi && (st & 1)) stage_body(st++, std::true_type{}, 1);
+            for (; st + 1 < s_hi; st += 2) {
+                stage_body(st, std::true_type{}, 0);
+                stage_body(st + 1, std::true_type{}, 1);
+            }
+            if (st < s_hi) stage_body(st, std::true_type{}, 0);
         }
-        if (st < s_hi) stage_body(st, std::true_type{}, 0);
+        for (int st = s_hi; st < nstage; ++st) stage_body(st, std::false_type{}, st & 1);
     }
-    for (int st = s_hi; st < nstage; ++st) stage_body(st, std::false_type{}, st & 1);
 
     if (FOLD) {
 #pragma unroll
         for (int t = 0; t < DG / kTile; ++t) G[t] *= gsign;
     }
-    if (xv) {
-        T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.H + hh) * n_x + x) * DG;
+    if (!xv) {  // rows past the batch's valid length get zero gradients
+#pragma unroll
+        for (int t = 0; t < DG / kTile; ++t) G[t] = f32x16{};
+    }
+    if (x < p.n_x) {
+        T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.Hout + ho) * p.n_x + x) * DG;
 #pragma unroll
         for (int t = 0; t < DG / kTile; ++t) {
 #pragma unroll
@@ -968,7 +1016,7 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 // mask high query blocks see the most keys and low key blocks are seen by the
 // most queries; for rectangular shapes the kind with the longer stream goes
 // first), walked in the order of block_order.
-template <typename T, int DT, int DS, bool CAUSAL, bool GS, bool FIRST>
+template <typename T, int DT, int DS, bool CAUSAL, bool GS, bool FIRST, bool GRP>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void streamkl_bwd_kernel(BwdParams pq,
                                                                                             BwdParams pk) {
     constexpr int STAGE = kBwdSub * (Tile<T, DT>::kBytes + Tile<T, DS>::kBytes);
@@ -997,8 +1045,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     }
     const bool dk = !(r - lo >= nk || (lo < nq && a_first(lo, r - lo)));
     const int idx = dk ? r - lo : nq - 1 - lo;
-    if (dk) bwd_block<T, DT, DS, CAUSAL, true, GS, FIRST>(pk, idx, bh, smem, rowv);
-    else bwd_block<T, DT, DS, CAUSAL, false, GS, FIRST>(pq, idx, bh, smem, rowv);
+    if (dk) bwd_block<T, DT, DS, CAUSAL, true, GS, FIRST, GRP>(pk, idx, bh, smem, rowv);
+    else bwd_block<T, DT, DS, CAUSAL, false, GS, FIRST, GRP>(pq, idx, bh, smem, rowv);
 }
 
 // ================================================================= host side
@@ -1006,9 +1054,36 @@ struct Shape {
     int B, H, n_q, n_k, d_t, d_s;
 };
 
+// Head counts of q_t, k_t, q_s, k_s and the per-batch length arrays of a
+// call (all H and null without a layout), checked.
+struct Heads {
+    int h[4];
+    const int *len_q, *len_k;
+};
+streamkl_status resolve_layout(const streamkl_layout *lay, int H, Heads &hd) {
+    hd.len_q = hd.len_k = nullptr;
+    for (int t = 0; t < 4; ++t) hd.h[t] = H;
+    if (!lay) return STREAMKL_OK;
+    const int given[4] = {lay->heads_q_t, lay->heads_k_t, lay->heads_q_s, lay->heads_k_s};
+    for (int t = 0; t < 4; ++t) {
+        if (given[t] < 0) return STREAMKL_ERR_INVALID;
+        hd.h[t] = given[t] ? given[t] : H;
+    }
+    // KL head h reads query head h / (H / Hq) and key head h / (H / Hk):
+    // Hq divides H and Hk divides Hq in each model (grouped keys)
+    for (int m = 0; m < 2; ++m) {
+        const int hq = hd.h[2 * m], hk = hd.h[2 * m + 1];
+        if (H % hq != 0 || hq % hk != 0) return STREAMKL_ERR_INVALID;
+    }
+    if (((uintptr_t)lay->seqlen_q) % 4 != 0 || ((uintptr_t)lay->seqlen_k) % 4 != 0) return STREAMKL_ERR_INVALID;
+    hd.len_q = lay->seqlen_q;
+    hd.len_k = lay->seqlen_k;
+    return STREAMKL_OK;
+}
+
 streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
                              streamkl_dtype dtype, const Shape &s, const int64_t *strides, float tau_t,
-                             float tau_s, int causal, int64_t st[12]) {
+                             float tau_s, int causal, const Heads &hd, int64_t st[12]) {
     if (!q_t || !k_t || !q_s || !k_s) return STREAMKL_ERR_INVALID;
     if (dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) return STREAMKL_ERR_INVALID;
     if (s.B < 1 || s.H < 1 || s.n_q < 1 || s.n_k < 1 || s.d_t < 1 || s.d_s < 1) return STREAMKL_ERR_INVALID;
@@ -1036,7 +1111,7 @@ streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, 
         } else {
             st[3 * t + 2] = dims[t];
             st[3 * t + 1] = (int64_t)ns[t] * dims[t];
-            st[3 * t + 0] = (int64_t)s.H * ns[t] * dims[t];
+            st[3 * t + 0] = (int64_t)hd.h[t] * ns[t] * dims[t];
         }
         if (((uintptr_t)ptrs[t]) % 16 != 0) return STREAMKL_ERR_INVALID;
         for (int k = 0; k < 3; ++k)
@@ -1077,9 +1152,10 @@ template <typename T, int DT, int DS, bool C>
 void launch_fwd(const FwdParams &p, int grid, hipStream_t s) {
     hipLaunchKernelGGL((streamkl_fwd_kernel<T, DT, DS, C>), dim3(grid), dim3(kThreads), 0, s, p);
 }
-template <typename T, int DT, int DS, bool C, bool GS, bool FIRST>
+template <typename T, int DT, int DS, bool C, bool GS, bool FIRST, bool GRP = false>
 void launch_bwd(const BwdParams &pq, const BwdParams &pk, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C, GS, FIRST>), dim3(grid), dim3(kThreads), 0, s, pq, pk);
+    hipLaunchKernelGGL((streamkl_bwd_kernel<T, DT, DS, C, GS, FIRST, GRP>), dim3(grid), dim3(kThreads), 0, s, pq,
+                       pk);
 }
 
 template <typename T, int DT, int DS>
@@ -1087,9 +1163,15 @@ fwd_launch_t pick_fwd2(int causal) {
     return causal ? launch_fwd<T, DT, DS, true> : launch_fwd<T, DT, DS, false>;
 }
 template <typename T, int DT, int DS>
-bwd_launch_t pick_bwd2(int causal, bool gs, bool first) {
-    // first-argument gradients take the per-row-weight form only (no scalar fold
-    // in key-major blocks), which halves their instantiations
+bwd_launch_t pick_bwd2(int causal, bool gs, bool first, bool grp) {
+    // grouped output heads and first-argument gradients take the per-row-weight
+    // form only (no scalar fold in key-major blocks), which halves their
+    // instantiations
+    if (grp) {
+        if (first) return causal ? launch_bwd<T, DT, DS, true, false, true, true>
+                                 : launch_bwd<T, DT, DS, false, false, true, true>;
+        return causal ? launch_bwd<T, DT, DS, true, false, false, true> : launch_bwd<T, DT, DS, false, false, false, true>;
+    }
     if (first) return causal ? launch_bwd<T, DT, DS, true, false, true> : launch_bwd<T, DT, DS, false, false, true>;
     if (gs) return causal ? launch_bwd<T, DT, DS, true, true, false> : launch_bwd<T, DT, DS, false, true, false>;
     return causal ? launch_bwd<T, DT, DS, true, false, false> : launch_bwd<T, DT, DS, false, false, false>;
@@ -1103,24 +1185,31 @@ fwd_launch_t pick_fwd1(int d_t, int d_s, int causal) {
     return nullptr;
 }
 template <typename T>
-bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool gs, bool first) {
-    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal, gs, first);
-    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal, gs, first);
-    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal, gs, first);
-    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal, gs, first);
+bwd_launch_t pick_bwd1(int d_t, int d_s, int causal, bool gs, bool first, bool grp) {
+    if (d_t == 64 && d_s == 64) return pick_bwd2<T, 64, 64>(causal, gs, first, grp);
+    if (d_t == 64 && d_s == 128) return pick_bwd2<T, 64, 128>(causal, gs, first, grp);
+    if (d_t == 128 && d_s == 64) return pick_bwd2<T, 128, 64>(causal, gs, first, grp);
+    if (d_t == 128 && d_s == 128) return pick_bwd2<T, 128, 128>(causal, gs, first, grp);
     return nullptr;
 }
 
 // The forward over keys [k_begin, k_end) in n_split equal chunks: finished
 // rows (state == null, one chunk) or raw online states ([n_split][rows][6]).
 streamkl_status fwd_common(const void *q_t, const void *k_t, const void *q_s, const void *k_s, streamkl_dtype dtype,
-                           int B, int H, int n_q, int n_k, int d_t, int d_s, const int64_t *strides, float tau_t,
-                           float tau_s, int causal, int k_begin, int k_end, int n_split, float *state,
-                           float *kl_rows, float *lse_t, float *lse_s, float *kl_sum, void *stream) {
+                           int B, int H, int n_q, int n_k, int d_t, int d_s, const int64_t *strides,
+                           const streamkl_layout *lay, float tau_t, float tau_s, int causal, int k_begin, int k_end,
+                           int n_split, float *state, float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
+                           void *stream) {
     const Shape s{B, H, n_q, n_k, d_t, d_s};
     FwdParams p{};
-    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, p.st);
+    if (B < 1 || H < 1) return STREAMKL_ERR_INVALID;
+    Heads hd;
+    streamkl_status rc = resolve_layout(lay, H, hd);
     if (rc != STREAMKL_OK) return rc;
+    rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, hd, p.st);
+    if (rc != STREAMKL_OK) return rc;
+    p.g_qt = H / hd.h[0]; p.g_kt = H / hd.h[1]; p.g_qs = H / hd.h[2]; p.g_ks = H / hd.h[3];
+    p.len_q = hd.len_q; p.len_k = hd.len_k;
     p.q_t = q_t; p.k_t = k_t; p.q_s = q_s; p.k_s = k_s;
     p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
     p.n_qblk = (n_q + kBlockX - 1) / kBlockX;
@@ -1158,21 +1247,31 @@ streamkl_status fwd_common(const void *q_t, const void *k_t, const void *q_s, co
 
 // Both backward entry points: gradients of sum_r g_r KL_r with respect to the
 // student (first = false, outputs d_s wide) or the teacher (first = true,
-// outputs d_t wide, needs the forward's per-row KL).
+// outputs d_t wide, needs the forward's per-row KL).  Without grouped heads
+// one launch holds the query-major and key-major blocks of every head; when
+// several KL heads feed one output head (grouped keys, or fewer query heads
+// in the differentiated model), each output block loops over its KL heads and
+// the two kinds go in two launches.
 streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
                            streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
-                           const int64_t *strides, float tau_t, float tau_s, int causal, const float *lse_t,
-                           const float *lse_s, const float *kl_rows, const float *grad_rows, float grad_scalar,
-                           void *dq_out, void *dk_out, bool first, void *stream) {
+                           const int64_t *strides, const streamkl_layout *lay, float tau_t, float tau_s, int causal,
+                           const float *lse_t, const float *lse_s, const float *kl_rows, const float *grad_rows,
+                           float grad_scalar, void *dq_out, void *dk_out, bool first, void *stream) {
     const Shape s{B, H, n_q, n_k, d_t, d_s};
+    if (B < 1 || H < 1) return STREAMKL_ERR_INVALID;
+    Heads hd;
+    streamkl_status rc = resolve_layout(lay, H, hd);
+    if (rc != STREAMKL_OK) return rc;
     int64_t st[12];
-    streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, st);
+    rc = check_common(q_t, k_t, q_s, k_s, dtype, s, strides, tau_t, tau_s, causal, hd, st);
     if (rc != STREAMKL_OK) return rc;
     if (!lse_t || !lse_s || !dq_out || !dk_out || (first && !kl_rows)) return STREAMKL_ERR_INVALID;
     if (!isfinite(grad_scalar)) return STREAMKL_ERR_INVALID;
     if (((uintptr_t)dq_out) % 16 != 0 || ((uintptr_t)dk_out) % 16 != 0) return STREAMKL_ERR_INVALID;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool bf = dtype == STREAMKL_BF16;
+    // tensor head counts in the order of BwdParams: teacher/student of the kind
+    const int hq_t = hd.h[0], hk_t = hd.h[1], hq_s = hd.h[2], hk_s = hd.h[3];
     BwdParams pp[2];
     for (int pass = 0; pass < 2; ++pass) {
         const bool dk = pass == 1;
@@ -1188,7 +1287,12 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
             p.st[6 + k] = st[3 * yi + k];
             p.st[9 + k] = st[3 * (2 + yi) + k];
         }
-        p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
+        const int ht[2] = {hq_t, hk_t}, hs2[2] = {hq_s, hk_s};
+        p.g_xt = H / ht[xi]; p.g_xs = H / hs2[xi]; p.g_yt = H / ht[yi]; p.g_ys = H / hs2[yi];
+        p.Hout = first ? ht[xi] : hs2[xi];
+        p.group = H / p.Hout;
+        p.len_q = hd.len_q; p.len_k = hd.len_k;
+        p.H = H; p.nheads = B * p.Hout; p.n_q = n_q; p.n_k = n_k;
         p.n_x = dk ? n_k : n_q;
         p.n_y = dk ? n_q : n_k;
         p.n_xblk = (p.n_x + kBlockX - 1) / kBlockX;
@@ -1197,23 +1301,40 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
         p.kl = kl_rows;
         p.out = dk ? dk_out : dq_out;
     }
-    {
+    const bool gs = grad_rows == nullptr;
+    const bool grp = pp[0].group > 1 || pp[1].group > 1;
+    bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal, gs, first, grp)
+                         : pick_bwd1<float>(d_t, d_s, causal, gs, first, grp);
+    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+    // work order: head-major or rank-major (block tiles at the full lengths)
+    auto order = [&](bool use_q, bool use_k, int64_t nheads) {
         int64_t mn = INT64_MAX, mx = 0, tot = 0;
-        for (int pass = 0; pass < 2; ++pass)
+        for (int pass = 0; pass < 2; ++pass) {
+            if (!(pass == 0 ? use_q : use_k)) continue;
             for (int xb = 0; xb < pp[pass].n_xblk; ++xb) {
-                const int64_t t = bwd_block_tiles(s, causal, pass == 1, xb);
+                const int64_t t = bwd_block_tiles(s, causal, pass == 1, xb) * pp[pass].group;
                 mn = std::min(mn, t);
                 mx = std::max(mx, t);
                 tot += t;
             }
-        pp[0].rank_major = pp[1].rank_major = want_rank_major(mn, mx, tot, (int64_t)B * H);
+        }
+        return want_rank_major(mn, mx, tot, nheads);
+    };
+    if (!grp) {
+        pp[0].rank_major = pp[1].rank_major = order(true, true, (int64_t)B * H);
+        fn(pp[0], pp[1], B * H * (pp[0].n_xblk + pp[1].n_xblk), hs);
+        if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+        return STREAMKL_OK;
     }
-    const bool gs = grad_rows == nullptr;
-    bwd_launch_t fn = bf ? pick_bwd1<bf16_t>(d_t, d_s, causal, gs, first)
-                         : pick_bwd1<float>(d_t, d_s, causal, gs, first);
-    if (!fn) return STREAMKL_ERR_UNSUPPORTED;
-    fn(pp[0], pp[1], B * H * (pp[0].n_xblk + pp[1].n_xblk), hs);
-    if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    for (int pass = 0; pass < 2; ++pass) {
+        BwdParams none = pp[1 - pass];
+        none.n_xblk = 0;
+        none.nheads = pp[pass].nheads;
+        pp[pass].rank_major = none.rank_major = order(pass == 0, pass == 1, pp[pass].nheads);
+        if (pass == 0) fn(pp[0], none, pp[0].nheads * pp[0].n_xblk, hs);
+        else fn(none, pp[1], pp[1].nheads * pp[1].n_xblk, hs);
+        if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+    }
     return STREAMKL_OK;
 }
 
@@ -1249,8 +1370,8 @@ streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, 
                              const int64_t *strides, float tau_t, float tau_s, int causal, float *kl_rows,
                              float *lse_t, float *lse_s, float *kl_sum, void *stream) {
     if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
-    return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, 0, n_k,
-                      1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
+    return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s, causal,
+                      0, n_k, 1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
 }
 
 int streamkl_fwd_split_count(int B, int H, int n_q, int n_k, int causal) {
@@ -1278,13 +1399,13 @@ streamkl_status streamkl_fwd_split(const void *q_t, const void *k_t, const void 
     if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
     if (n_split < 1 || n_split > kMaxSplit) return STREAMKL_ERR_INVALID;
     if (n_split == 1)
-        return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, 0,
-                          n_k, 1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
+        return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s,
+                          causal, 0, n_k, 1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
     if (B < 1 || H < 1 || n_q < 1) return STREAMKL_ERR_INVALID;
     if (!workspace || ((uintptr_t)workspace) % 16 != 0) return STREAMKL_ERR_INVALID;
     if (workspace_bytes < streamkl_fwd_split_workspace_size(B, H, n_q, n_split)) return STREAMKL_ERR_WORKSPACE;
     float *state = static_cast<float *>(workspace);
-    streamkl_status rc = fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s,
+    streamkl_status rc = fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s,
                                     causal, 0, n_k, n_split, state, nullptr, nullptr, nullptr, nullptr, stream);
     if (rc != STREAMKL_OK) return rc;
     return streamkl_fwd_merge(state, n_split, (int64_t)B * H * n_q, tau_t, tau_s, kl_rows, lse_t, lse_s, kl_sum,
@@ -1298,8 +1419,8 @@ streamkl_status streamkl_fwd_partial(const void *q_t, const void *k_t, const voi
     if (!state || ((uintptr_t)state) % 16 != 0) return STREAMKL_ERR_INVALID;
     if (k_begin < 0 || k_end > n_k || k_begin >= k_end) return STREAMKL_ERR_INVALID;
     if (k_begin % kBN != 0 || (k_end % kBN != 0 && k_end != n_k)) return STREAMKL_ERR_INVALID;
-    return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, k_begin,
-                      k_end, 1, state, nullptr, nullptr, nullptr, nullptr, stream);
+    return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s, causal,
+                      k_begin, k_end, 1, state, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 streamkl_status streamkl_fwd_merge(const float *states, int n_states, int64_t rows, float tau_t, float tau_s,
@@ -1323,8 +1444,8 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
                              const int64_t *strides, float tau_t, float tau_s, int causal, const float *lse_t,
                              const float *lse_s, const float *grad_rows, float grad_scalar, void *dq_s,
                              void *dk_s, void *stream) {
-    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, lse_t,
-                      lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, stream);
+    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s, causal,
+                      lse_t, lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, stream);
 }
 
 streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
@@ -1333,8 +1454,37 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
                                      const float *lse_t, const float *lse_s, const float *kl_rows,
                                      const float *grad_rows, float grad_scalar, void *dq_t, void *dk_t,
                                      void *stream) {
-    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal, lse_t,
-                      lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, stream);
+    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s, causal,
+                      lse_t, lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, stream);
+}
+
+streamkl_status streamkl_fwd_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                const int64_t *strides, const streamkl_layout *layout, float tau_t, float tau_s,
+                                int causal, float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
+                                void *stream) {
+    if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
+    return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, layout, tau_t, tau_s, causal, 0,
+                      n_k, 1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
+}
+
+streamkl_status streamkl_bwd_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                const int64_t *strides, const streamkl_layout *layout, float tau_t, float tau_s,
+                                int causal, const float *lse_t, const float *lse_s, const float *grad_rows,
+                                float grad_scalar, void *dq_s, void *dk_s, void *stream) {
+    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, layout, tau_t, tau_s, causal,
+                      lse_t, lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, stream);
+}
+
+streamkl_status streamkl_bwd_teacher_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                        streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                        const int64_t *strides, const streamkl_layout *layout, float tau_t,
+                                        float tau_s, int causal, const float *lse_t, const float *lse_s,
+                                        const float *kl_rows, const float *grad_rows, float grad_scalar, void *dq_t,
+                                        void *dk_t, void *stream) {
+    return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, layout, tau_t, tau_s, causal,
+                      lse_t, lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, stream);
 }
 
 }  // extern "C"

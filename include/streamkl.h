@@ -202,6 +202,63 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
                                      void *dq_t, void *dk_t, void *stream);
 
 /*
+ * Grouped heads and per-batch lengths.  The pages define the divergence per
+ * query row of one teacher and one student attention map and say nothing of
+ * how heads pair up when the two models, or the queries and keys of one
+ * model, have different head counts; these entry points take the plainest
+ * reading, the grouped-key convention.  There are H KL heads (the per-row
+ * outputs are [B, H, n_q]); KL head h compares teacher query head
+ * h / (H / heads_q_t) against student query head h / (H / heads_q_s), each
+ * attending over its own model's key head h / (H / heads_k), so a model
+ * with fewer query heads than H is broadcast over consecutive KL heads, and
+ * keys are shared by consecutive query heads as in grouped-query attention.
+ * Every heads_q divides H and every heads_k divides its model's heads_q.
+ *
+ * Tensors keep their own head counts: q_t [B, heads_q_t, n_q, d_t], k_t
+ * [B, heads_k_t, n_k, d_t], q_s [B, heads_q_s, n_q, d_s], k_s [B, heads_k_s,
+ * n_k, d_s]; default strides are contiguous in those shapes.  The gradient of
+ * a shared head is the sum over the KL heads that read it: dq_s [B,
+ * heads_q_s, n_q, d_s], dk_s [B, heads_k_s, n_k, d_s] (dq_t, dk_t likewise
+ * with the teacher's counts).
+ *
+ * Padding: seqlen_q / seqlen_k (device int32 [B], NULL = n_q / n_k) give the
+ * valid query rows and keys of each batch inside the padded n_q / n_k
+ * (values are clamped to [0, n_q] / [0, n_k]).  Keys past seqlen_k[b] are
+ * masked from both softmaxes; rows past seqlen_q[b] are empty.  The causal
+ * mask is bottom-right aligned within the valid lengths
+ * (j <= i + seqlen_k[b] - seqlen_q[b]).  An empty row (past the valid length,
+ * or left with no allowed key) has KL 0 and LSEs 0, and contributes no
+ * gradient; gradient rows past the valid lengths are written as 0.
+ */
+typedef struct {
+    int heads_q_t, heads_k_t, heads_q_s, heads_k_s;  /* 0 means H */
+    const int32_t *seqlen_q, *seqlen_k;               /* device [B], 4-byte aligned, or NULL */
+} streamkl_layout;
+
+/* streamkl_fwd with a layout (NULL layout = streamkl_fwd).  INVALID also for a
+ * head count that is negative or breaks the divisibility above. */
+streamkl_status streamkl_fwd_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                const int64_t *strides, const streamkl_layout *layout, float tau_t, float tau_s,
+                                int causal, float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
+                                void *stream);
+
+/* streamkl_bwd with a layout: dq_s, dk_s in the student's head counts. */
+streamkl_status streamkl_bwd_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                const int64_t *strides, const streamkl_layout *layout, float tau_t, float tau_s,
+                                int causal, const float *lse_t, const float *lse_s, const float *grad_rows,
+                                float grad_scalar, void *dq_s, void *dk_s, void *stream);
+
+/* streamkl_bwd_teacher with a layout: dq_t, dk_t in the teacher's head counts. */
+streamkl_status streamkl_bwd_teacher_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                        streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                        const int64_t *strides, const streamkl_layout *layout, float tau_t,
+                                        float tau_s, int causal, const float *lse_t, const float *lse_s,
+                                        const float *kl_rows, const float *grad_rows, float grad_scalar, void *dq_t,
+                                        void *dk_t, void *stream);
+
+/*
  * Vocabulary-logit KL at temperature.  The distillation loss of "Lecture 05 -
  * Where It All Lands", section 3.1, applied to output logits: for every row r
  * of the teacher and student logit matrices z_t, z_s ([rows, V]),

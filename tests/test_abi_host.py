@@ -213,3 +213,35 @@ def test_vocab_binding_fails_loudly_without_device_tensors():
         skl.streamkl_vocab_fwd(z, z)
     with pytest.raises(ValueError):
         skl.vocab_kl(z, z)
+
+
+def test_layout_entry_points_reject_bad_layouts_before_any_hip_call():
+    lib = skl.load_library()
+
+    def fwd(hq_t=0, hk_t=0, hq_s=0, hk_s=0, sq=None, sk=None, H=8):
+        lay = skl.StreamKLLayout(hq_t, hk_t, hq_s, hk_s, sq, sk)
+        return lib.streamkl_fwd_ex(A, A + 0x100000, A + 0x200000, A + 0x300000, skl.STREAMKL_BF16, 2, H, 100, 300,
+                                   128, 64, None, ctypes.byref(lay), 0.088, 0.125, 0, A + 0x400000, A + 0x500000,
+                                   A + 0x600000, None, None)
+    assert fwd(hq_t=-1) == INV
+    assert fwd(hq_s=3) == INV           # 3 does not divide H = 8
+    assert fwd(hq_t=4, hk_t=8) == INV   # more key heads than query heads
+    assert fwd(hq_s=4, hk_s=3) == INV   # 3 does not divide 4
+    assert fwd(sq=A + 2) == INV         # misaligned length array
+    assert fwd(sk=A + 6) == INV
+    assert fwd(hq_t=4, hk_t=2, hq_s=8, hk_s=1, H=0) == INV
+
+    def bwd(first, **kw):
+        lay = skl.StreamKLLayout(kw.get("hq_t", 0), kw.get("hk_t", 0), kw.get("hq_s", 0), kw.get("hk_s", 0), None,
+                                 None)
+        if first:
+            return lib.streamkl_bwd_teacher_ex(A, A + 0x100000, A + 0x200000, A + 0x300000, skl.STREAMKL_BF16, 2, 8,
+                                               100, 300, 128, 64, None, ctypes.byref(lay), 0.088, 0.125, 0, A, A,
+                                               kw.get("kl", A), None, 1.0, A + 0x700000, A + 0x800000, None)
+        return lib.streamkl_bwd_ex(A, A + 0x100000, A + 0x200000, A + 0x300000, skl.STREAMKL_BF16, 2, 8, 100, 300,
+                                   128, 64, None, ctypes.byref(lay), 0.088, 0.125, 0, A, A, None, 1.0,
+                                   kw.get("dq", A + 0x700000), A + 0x800000, None)
+    assert bwd(False, hk_s=5) == INV
+    assert bwd(False, hk_s=2, dq=None) == INV
+    assert bwd(True, hk_t=2, kl=None) == INV
+    assert bwd(True, hq_t=16) == INV    # 16 does not divide H = 8

@@ -1,0 +1,172 @@
+"""GPU parity of grouped heads and per-batch lengths (streamkl_fwd_ex,
+streamkl_bwd_ex, streamkl_bwd_teacher_ex) against the fp64 oracle.
+
+The reference is the oracle applied to the definition of the layout: KL head h
+reads head h // (H / heads) of each tensor (np.repeat over the head axis), each
+batch is cut to its valid lengths (under a causal mask with more valid
+queries than keys, the first rows have no key and are empty), and the gradient
+of a shared head is the sum over the KL heads that read it."""
+import numpy as np
+import pytest
+
+import attention_kl_divergence_amd as skl
+import oracle
+from tests.gpu_util import check_grad, check_kl, check_lse, check_sum
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _round_bf16(a):
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def _draw(seed, B, heads, n_q, n_k, d_t, d_s, dtype, sigma=0.3):
+    """Teacher and student tensors with their own head counts (student = a
+    noisy copy of the teacher where the head counts allow)."""
+    rng = np.random.default_rng(seed)
+    hq_t, hk_t, hq_s, hk_s = heads
+    x = {"q_t": rng.standard_normal((B, hq_t, n_q, d_t), dtype=np.float32),
+         "k_t": rng.standard_normal((B, hk_t, n_k, d_t), dtype=np.float32),
+         "q_s": rng.standard_normal((B, hq_s, n_q, d_s), dtype=np.float32),
+         "k_s": rng.standard_normal((B, hk_s, n_k, d_s), dtype=np.float32)}
+    if d_t == d_s and hq_t == hq_s:
+        x["q_s"] = (x["q_t"] + np.float32(sigma) * x["q_s"]).astype(np.float32)
+    if d_t == d_s and hk_t == hk_s:
+        x["k_s"] = (x["k_t"] + np.float32(sigma) * x["k_s"]).astype(np.float32)
+    if dtype == "bf16":
+        x = {k: _round_bf16(v) for k, v in x.items()}
+    return x
+
+
+def _reference(x, H, tau_t, tau_s, causal, lq=None, lk=None, g=None):
+    xo = {k: np.repeat(v.astype(np.float64), H // v.shape[1], axis=1) for k, v in x.items()}
+    B, _, n_q, d_t = xo["q_t"].shape
+    n_k, d_s = xo["k_t"].shape[2], xo["q_s"].shape[3]
+    kl = np.zeros((B, H, n_q)); lt = np.zeros_like(kl); ls = np.zeros_like(kl)
+    dqs = np.zeros((B, H, n_q, d_s)); dks = np.zeros((B, H, n_k, d_s))
+    dqt = np.zeros((B, H, n_q, d_t)); dkt = np.zeros((B, H, n_k, d_t))
+    for b in range(B):
+        nq = n_q if lq is None else int(lq[b])
+        nk = n_k if lk is None else int(lk[b])
+        q0 = nq - nk if (causal and nq > nk) else 0  # rows before q0 have no allowed key
+        if nq - q0 <= 0 or nk <= 0:
+            continue
+        a = [xo["q_t"][b:b + 1, :, q0:nq], xo["k_t"][b:b + 1, :, :nk], xo["q_s"][b:b + 1, :, q0:nq],
+             xo["k_s"][b:b + 1, :, :nk]]
+        a = [np.ascontiguousarray(t) for t in a]
+        rkl, rlt, rls, _ = oracle.fwd(*a, tau_t, tau_s, causal)
+        kl[b, :, q0:nq], lt[b, :, q0:nq], ls[b, :, q0:nq] = rkl[0], rlt[0], rls[0]
+        gb = None if g is None else np.ascontiguousarray(g[b:b + 1, :, q0:nq], dtype=np.float64)
+        rdq, rdk = oracle.bwd(*a, tau_t, tau_s, causal, g=gb)
+        dqs[b, :, q0:nq], dks[b, :, :nk] = rdq[0], rdk[0]
+        tdq, tdk = oracle.bwd_teacher(*a, tau_t, tau_s, causal, g=gb)
+        dqt[b, :, q0:nq], dkt[b, :, :nk] = tdq[0], tdk[0]
+
+    def fold(gr, h):
+        return gr.reshape(gr.shape[0], h, H // h, *gr.shape[2:]).sum(axis=2)
+    return dict(kl=kl, lse_t=lt, lse_s=ls, dq_s=fold(dqs, x["q_s"].shape[1]), dk_s=fold(dks, x["k_s"].shape[1]),
+                dq_t=fold(dqt, x["q_t"].shape[1]), dk_t=fold(dkt, x["k_t"].shape[1]))
+
+
+def _gpu(x, dtype, causal, lq=None, lk=None, g=None, g_scalar=1.0, tau=(None, None)):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(tdt).cuda() for k, v in x.items()}
+    sq = None if lq is None else torch.tensor(lq, dtype=torch.int32, device="cuda")
+    sk = None if lk is None else torch.tensor(lk, dtype=torch.int32, device="cuda")
+    args = (d["q_t"], d["k_t"], d["q_s"], d["k_s"])
+    kl, lt, ls, tot = skl.streamkl_fwd(*args, tau[0], tau[1], causal, seqlen_q=sq, seqlen_k=sk)
+    gt = None if g is None else torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).cuda()
+    dqs, dks = skl.streamkl_bwd(*args, lt, ls, grad_rows=gt, grad_scalar=g_scalar, tau_t=tau[0], tau_s=tau[1],
+                                causal=causal, seqlen_q=sq, seqlen_k=sk)
+    dqt, dkt = skl.streamkl_bwd_teacher(*args, lt, ls, kl, grad_rows=gt, grad_scalar=g_scalar, tau_t=tau[0],
+                                        tau_s=tau[1], causal=causal, seqlen_q=sq, seqlen_k=sk)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    return dict(kl=f(kl), lse_t=f(lt), lse_s=f(ls), sum=float(tot.item()), dq_s=f(dqs), dk_s=f(dks), dq_t=f(dqt),
+                dk_t=f(dkt))
+
+
+# (name, B, heads (q_t, k_t, q_s, k_s), n_q, n_k, d_t, d_s, dtype, causal, lengths (q, k) or None)
+CASES = [
+    ("student_gqa4_bf16", 2, (8, 8, 8, 2), 200, 300, 128, 64, "bf16", False, None),
+    ("both_gqa_f32_causal", 2, (4, 2, 4, 1), 130, 130, 64, 64, "f32", True, None),
+    ("student_fewer_q_heads_bf16", 1, (8, 8, 4, 2), 160, 200, 128, 128, "bf16", False, None),
+    ("teacher_fewer_q_heads_bf16_causal", 2, (2, 1, 4, 4), 100, 140, 64, 128, "bf16", True, None),
+    ("lengths_bf16", 3, (4, 4, 4, 4), 256, 320, 128, 128, "bf16", False, ([200, 17, 0], [300, 40, 5])),
+    ("lengths_causal_f32", 3, (2, 2, 2, 2), 160, 192, 64, 64, "f32", True, ([150, 64, 100], [192, 64, 37])),
+    ("lengths_gqa_bf16_causal", 2, (8, 4, 4, 1), 200, 256, 128, 64, "bf16", True, ([199, 60], [256, 61])),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_grouped_and_lengths_match_oracle(case):
+    name, B, heads, n_q, n_k, d_t, d_s, dtype, causal, lens = case
+    print(f"[grouped] {case}", flush=True)
+    H = max(heads[0], heads[2])
+    x = _draw(100 + [c[0] for c in CASES].index(name), B, heads, n_q, n_k, d_t, d_s, dtype)
+    lq, lk = (None, None) if lens is None else lens
+    # per-row upstream weights of both signs: shared query heads fold KL heads of different signs
+    g = np.random.default_rng(7).standard_normal((B, H, n_q)).astype(np.float32)
+    tau_t, tau_s = float(np.float32(1 / np.sqrt(d_t))), float(np.float32(1 / np.sqrt(d_s)))
+    out = _gpu(x, dtype, causal, lq, lk, g=g)
+    ref = _reference(x, H, tau_t, tau_s, causal, lq, lk, g=g)
+    check_kl(out["kl"], ref["kl"], dtype, f"{name} kl")
+    check_lse(out["lse_t"], ref["lse_t"], dtype, f"{name} lse_t")
+    check_lse(out["lse_s"], ref["lse_s"], dtype, f"{name} lse_s")
+    check_sum(out["sum"], ref["kl"], dtype)
+    for k in ("dq_s", "dk_s", "dq_t", "dk_t"):
+        assert out[k].shape == ref[k].shape, (k, out[k].shape, ref[k].shape)
+        check_grad(out[k], ref[k], dtype, f"{name} {k}")
+    if lens is not None:
+        # rows and keys past the valid lengths: KL 0 and zero gradients, exactly
+        for b in range(B):
+            assert not np.any(out["kl"][b, :, lq[b]:]) and not np.any(out["lse_t"][b, :, lq[b]:])
+            assert not np.any(out["dq_s"][b, :, lq[b]:]) and not np.any(out["dk_s"][b, :, lk[b]:])
+            assert not np.any(out["dq_t"][b, :, lq[b]:]) and not np.any(out["dk_t"][b, :, lk[b]:])
+
+
+def test_grouped_scalar_upstream_gradient():
+    B, heads, n_q, n_k = 2, (8, 8, 4, 2), 96, 160
+    x = _draw(11, B, heads, n_q, n_k, 128, 128, "bf16")
+    out = _gpu(x, "bf16", False, g=None, g_scalar=-1.5)
+    ref = _reference(x, 8, float(np.float32(1 / np.sqrt(128))), float(np.float32(1 / np.sqrt(128))), False,
+                     g=np.full((B, 8, n_q), -1.5))
+    for k in ("dq_s", "dk_s", "dq_t", "dk_t"):
+        check_grad(out[k], ref[k], "bf16", f"scalar {k}")
+
+
+def test_equal_heads_through_the_layout_match_the_plain_entry_points():
+    """A layout that changes nothing (equal heads, full lengths) gives the same
+    bits as the plain entry points."""
+    B, heads, n_q, n_k = 2, (4, 4, 4, 4), 130, 200
+    x = _draw(12, B, heads, n_q, n_k, 128, 128, "bf16")
+    d = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    args = (d["q_t"], d["k_t"], d["q_s"], d["k_s"])
+    full_q = torch.full((B,), n_q, dtype=torch.int32, device="cuda")
+    full_k = torch.full((B,), n_k, dtype=torch.int32, device="cuda")
+    a = skl.streamkl_fwd(*args, causal=True, split=1)
+    b = skl.streamkl_fwd(*args, causal=True, seqlen_q=full_q, seqlen_k=full_k)
+    ga = skl.streamkl_bwd(*args, a[1], a[2], causal=True)
+    gb = skl.streamkl_bwd(*args, b[1], b[2], causal=True, seqlen_q=full_q, seqlen_k=full_k)
+    torch.cuda.synchronize()
+    for u, v in zip(tuple(a[:3]) + tuple(ga), tuple(b[:3]) + tuple(gb)):
+        assert torch.equal(u, v)
+
+
+def test_grouped_autograd():
+    B, heads, n_q, n_k = 1, (4, 4, 4, 2), 64, 96
+    x = _draw(13, B, heads, n_q, n_k, 64, 64, "f32")
+    d = {k: torch.from_numpy(v).cuda().requires_grad_(k.endswith("_s")) for k, v in x.items()}
+    sk = torch.tensor([80], dtype=torch.int32, device="cuda")
+    kl = skl.attention_kl(d["q_t"], d["k_t"], d["q_s"], d["k_s"], seqlen_k=sk)
+    kl.sum().backward()
+    torch.cuda.synchronize()
+    t = float(np.float32(1 / 8.0))
+    ref = _reference(x, 4, t, t, False, lk=[80], g=np.ones((B, 4, n_q)))
+    check_kl(kl.detach().cpu().numpy(), ref["kl"], "f32", "autograd kl")
+    check_grad(d["q_s"].grad.cpu().numpy(), ref["dq_s"], "f32", "autograd dq_s")
+    check_grad(d["k_s"].grad.cpu().numpy(), ref["dk_s"], "f32", "autograd dk_s")
+    assert d["k_s"].grad.shape == (B, 2, n_k, 64)

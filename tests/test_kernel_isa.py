@@ -44,8 +44,9 @@ def test_every_kernel_barrier_drains_vmcnt_first(asm):
     no vector-memory load is issued between it and the barrier."""
     kernels = list(_kernels(asm))
     # {bf16, f32} x {64, 128}^2 x {causal, not}: 16 forward kernels, 32 student
-    # backward kernels ({scalar, per-row} upstream gradient) and 16 teacher ones
-    assert len(kernels) == 64
+    # backward kernels ({scalar, per-row} upstream gradient), 16 teacher ones,
+    # and 32 grouped-head backward kernels (student and teacher)
+    assert len(kernels) == 96
     for name, body in kernels:
         nbar = 0
         for k, line in enumerate(body):
@@ -70,9 +71,12 @@ def test_no_spills_in_the_mfma_loops(asm):
     text = "\n".join(asm)
     found = list(re.finditer(r"\.name:\s+(_ZN12_GLOBAL__N_1\d+streamkl_\w+)[\s\S]*?"
                              r"\.private_segment_fixed_size:\s+(\d+)", text))
-    assert len(found) == 66  # 64 forward/backward instantiations + the sum and merge kernels
+    assert len(found) == 98  # 96 forward/backward instantiations + the sum and merge kernels
     for m in found:
-        assert int(m.group(2)) <= 64, m.group(1)
+        # grouped-head backward kernels (last template flag GRP = 1) keep more
+        # state across their head loop and spill at the head boundaries
+        grouped = m.group(1).endswith("Lb1EEEvNS_9BwdParamsES1_")
+        assert int(m.group(2)) <= (256 if grouped else 64), m.group(1)
     for name, body in _kernels(asm):
         block, mfma, scratch = "entry", 0, 0
         for line in body + [".LBBend:"]:
