@@ -24,11 +24,14 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        timed in its own loop after the headline steps)
        python bench.py --copy-calibration MiB   (a plain device copy of known
                        size, run under the same HBM byte counters to scale them)
+       python bench.py --student-kv-heads N  (adds the grouped-key forward and
+                       backward: N student key heads shared by H / N query heads)
        python bench.py --vocab [--vocab-workload NAME] [--cpu-rows N]
                        (the vocabulary-logit KL: forward + student backward per
                        step, the fused launch timed beside it; HBM roofline)
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -299,6 +302,8 @@ def main():
                     help="key splits of the forward (default: the library's suggestion for the shape)")
     ap.add_argument("--teacher-grads", action="store_true",
                     help="also time the first-argument (teacher) backward, outside the headline step")
+    ap.add_argument("--student-kv-heads", type=int, default=0, metavar="N",
+                    help="also time the grouped-key forward and backward with N student key heads")
     ap.add_argument("--vocab", action="store_true",
                     help="measure the vocabulary-logit KL instead (its own JSON line)")
     ap.add_argument("--vocab-workload", default="kd_logits_4k_128k")
@@ -451,6 +456,45 @@ def main():
         res["bwd_teacher_ms"] = round(float(np.mean(t_t)), 4)
         res["bwd_teacher_tflops"] = round(Ft / (np.mean(t_t) * 1e-3) / 1e12, 2)
         print(f"[bench] teacher bwd {np.mean(t_t):.3f} ms ({res['bwd_teacher_tflops']:.1f} TF/s)",
+              file=sys.stderr, flush=True)
+    if args.student_kv_heads:
+        # grouped student keys: the first N key heads of K_s shared by H / N query heads each
+        nkv = args.student_kv_heads
+        ks_g = d["k_s"][:, :nkv].contiguous()
+        lay = skl.StreamKLLayout(0, 0, 0, nkv, None, None)
+        dkg = torch.empty((B, nkv, w.n_k, w.d_s), dtype=tdt, device=dev)
+
+        def fwd_g():
+            rc = lib.streamkl_fwd_ex(ptr["q_t"], ptr["k_t"], ptr["q_s"], ks_g.data_ptr(), code, B, H, w.n_q, w.n_k,
+                                     w.d_t, w.d_s, None, ctypes.byref(lay), w.tau_t, w.tau_s, int(w.causal),
+                                     kl.data_ptr(), lt.data_ptr(), ls.data_ptr(), tot.data_ptr(), sp)
+            if rc:
+                raise RuntimeError(skl.status_string(rc))
+
+        def bwd_g():
+            rc = lib.streamkl_bwd_ex(ptr["q_t"], ptr["k_t"], ptr["q_s"], ks_g.data_ptr(), code, B, H, w.n_q, w.n_k,
+                                     w.d_t, w.d_s, None, ctypes.byref(lay), w.tau_t, w.tau_s, int(w.causal),
+                                     lt.data_ptr(), ls.data_ptr(), None, 1.0, dq.data_ptr(), dkg.data_ptr(), sp)
+            if rc:
+                raise RuntimeError(skl.status_string(rc))
+        for _ in range(args.warmup):
+            fwd_g()
+            bwd_g()
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for e in gev:
+            e[0].record(stream)
+            fwd_g()
+            e[1].record(stream)
+            bwd_g()
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        g_f = np.array([e[0].elapsed_time(e[1]) for e in gev])
+        g_b = np.array([e[1].elapsed_time(e[2]) for e in gev])
+        res["grouped"] = {"student_kv_heads": nkv, "fwd_ms": round(float(np.mean(g_f)), 4),
+                          "bwd_ms": round(float(np.mean(g_b)), 4),
+                          "fwd_tflops": round(F / (np.mean(g_f) * 1e-3) / 1e12, 2),
+                          "bwd_tflops": round(Bw / (np.mean(g_b) * 1e-3) / 1e12, 2)}
+        print(f"[bench] grouped student keys ({nkv} heads): fwd {np.mean(g_f):.3f} ms, bwd {np.mean(g_b):.3f} ms",
               file=sys.stderr, flush=True)
     if not args.no_baseline_mem:
         bpk = materialized_baseline_peak(w, d, torch)
