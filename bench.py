@@ -51,18 +51,17 @@ def flops(w):
     return 2.0 * pairs * (w.d_t + w.d_s), 2.0 * pairs * (w.d_t + 3 * w.d_s)
 
 
-def materialized_baseline_peak(w, d, torch):
-    """Peak HBM of the materialize-then-reduce pattern (log_softmax of both
-    full score matrices, elementwise KL, sum, autograd backward) for one
-    (batch, head) slice, scaled to the whole batch.  Returns bytes or None."""
+def materialized_baseline(w, d, torch):
+    """The materialize-then-reduce pattern (fp32 scores, log_softmax of both
+    full score matrices, elementwise KL, sum, autograd backward) on one
+    (batch, head) slice: its peak HBM and its fwd+bwd time, both scaled to the
+    whole batch.  Returns (bytes, ms) or (None, None) when it does not fit."""
     import math
-    try:
+
+    def one():
         q_t, k_t = d["q_t"][:1, :1].float(), d["k_t"][:1, :1].float()
         q_s = d["q_s"][:1, :1].float().clone().requires_grad_(True)
         k_s = d["k_s"][:1, :1].float().clone().requires_grad_(True)
-        torch.cuda.synchronize()
-        base = torch.cuda.memory_allocated()
-        torch.cuda.reset_peak_memory_stats()
         st = (q_t @ k_t.transpose(-1, -2).contiguous()) * w.tau_t
         ss = (q_s @ k_s.transpose(-1, -2).contiguous()) * w.tau_s
         if w.causal:
@@ -74,14 +73,25 @@ def materialized_baseline_peak(w, d, torch):
         pt = lpt.exp()
         klr = torch.where(pt > 0, pt * (lpt - lps), torch.zeros_like(pt)).sum(-1)
         klr.sum().backward()
+    try:
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        one()  # also the warm-up of the timed run
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
-        del st, ss, lpt, lps, pt, klr, q_s, k_s
         torch.cuda.empty_cache()
-        return int(peak) * w.B * w.H
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        one()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        torch.cuda.empty_cache()
+        return int(peak) * w.B * w.H, ms * w.B * w.H
     except RuntimeError:  # out of memory
         torch.cuda.empty_cache()
-        return None
+        return None, None
 
 
 def kernel_source_hash(src="streamkl.hip"):
@@ -425,6 +435,8 @@ def main():
                    "fwd_key_splits": int(n_split)},
         "pct_peak": round(100.0 * value / peak, 2),
         "fwd_ms": round(float(np.mean(t_f)), 4), "bwd_ms": round(float(np.mean(t_b)), 4),
+        "fwd_ms_median": round(float(np.median(t_f)), 4), "bwd_ms_median": round(float(np.median(t_b)), 4),
+        "fwd_ms_min": round(float(np.min(t_f)), 4), "bwd_ms_min": round(float(np.min(t_b)), 4),
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
         "extra_hbm_bytes": extra_bytes,
         "input_bytes": in_bytes,
@@ -497,8 +509,11 @@ def main():
         print(f"[bench] grouped student keys ({nkv} heads): fwd {np.mean(g_f):.3f} ms, bwd {np.mean(g_b):.3f} ms",
               file=sys.stderr, flush=True)
     if not args.no_baseline_mem:
-        bpk = materialized_baseline_peak(w, d, torch)
+        bpk, bms = materialized_baseline(w, d, torch)
         res["materialized_baseline_peak_bytes"] = bpk
+        # the same pattern's fwd+bwd time, one (batch, head) slice timed and scaled by B H (context only)
+        res["materialized_baseline_ms_extrapolated"] = round(bms, 2) if bms is not None else None
+        res["speedup_vs_materialized"] = round(bms / ms_step, 2) if bms is not None else None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded slice", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
