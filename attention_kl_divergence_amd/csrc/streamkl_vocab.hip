@@ -25,8 +25,11 @@
 //  * the backward recomputes p and q from the saved log-normalisers and writes
 //    dz_s (and dz_t) with 16-byte stores; no workspace, no atomics.
 // Rows that are not 16-byte aligned (V or the leading dimension not a multiple
-// of 8, or a misaligned base) take a generic path with element loads, still
-// coalesced across the wave.
+// of 8, or a misaligned base) stream their aligned body the same way when the
+// rows of all operands start equally far from a 16-byte boundary (as two
+// contiguous [rows, V] matrices do), with a few scalar logits before and
+// after it; otherwise they take an element path, still coalesced across the
+// wave.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -211,45 +214,80 @@ struct VocabParams {
 
 // Lane-subset pass of one row: the lane's state over its logits.
 // LPR lanes share the row; `li` is this lane's index among them.
+// Elements before the first 16-byte boundary of a row (p is element-aligned).
+template <typename T> __device__ inline int head_elems(const T *p) {
+    return (int)(((16u - ((unsigned)(uintptr_t)p & 15u)) & 15u) / sizeof(T));
+}
+
+// Vector steps over a 16-byte aligned run of n (a multiple of 8) logits.
+template <typename T, int LPR, int kUnroll>
+__device__ inline void state_vec(const T *zt, const T *zs, int n, float c, int li, VState &s) {
+    using Io = VIo<T>;
+    const int nst = n / kStep;
+    int k = li;
+    for (; k + (kUnroll - 1) * LPR < nst; k += kUnroll * LPR) {
+        typename Io::Raw a[kUnroll], b[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            a[u] = Io::load(zt + (int64_t)(k + u * LPR) * kStep);
+            b[u] = Io::load(zs + (int64_t)(k + u * LPR) * kStep);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float x[8], y[8];
+            Io::widen(a[u], x);
+            Io::widen(b[u], y);
+            vs_fold8(s, x, y, c);
+        }
+    }
+    for (; k < nst; k += LPR) {
+        float x[8], y[8];
+        Io::widen(Io::load(zt + (int64_t)k * kStep), x);
+        Io::widen(Io::load(zs + (int64_t)k * kStep), y);
+        vs_fold8(s, x, y, c);
+    }
+}
+
+// Lane-subset pass of one row: the lane's state over its logits.
+// LPR lanes share the row; `li` is this lane's index among them.  VEC: the
+// row is 16-byte aligned and V a multiple of 8.  Otherwise, when both rows
+// start equally far from a 16-byte boundary (always so for two contiguous
+// [rows, V] matrices with aligned bases), lanes 0-7 take the head before the
+// first boundary and lanes 8-15 the tail after the last whole step, one logit
+// each, and the aligned body is streamed as in the vector case; rows without
+// that match are read one logit per lane and step.
 template <typename T, bool VEC, int LPR, int kUnroll = kUnrollState>
 __device__ inline void row_state(const T *zt, const T *zs, int V, float c, int li, VState &s) {
     using Io = VIo<T>;
     if (VEC) {
-        const int nst = V / kStep;
-        int k = li;
-        for (; k + (kUnroll - 1) * LPR < nst; k += kUnroll * LPR) {
-            typename Io::Raw a[kUnroll], b[kUnroll];
+        state_vec<T, LPR, kUnroll>(zt, zs, V, c, li, s);
+        return;
+    }
+    const int h = head_elems(zt);
+    if (h == head_elems(zs) && h <= V) {
+        const int body = ((V - h) / kStep) * kStep;
+        float x[8], y[8];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                a[u] = Io::load(zt + (int64_t)(k + u * LPR) * kStep);
-                b[u] = Io::load(zs + (int64_t)(k + u * LPR) * kStep);
-            }
+        for (int j = 1; j < 8; ++j) x[j] = y[j] = kPad;
+        int v = -1;
+        if (li < 8) v = li < h ? li : -1;
+        else if (li < 16) v = h + body + (li - 8) < V ? h + body + (li - 8) : -1;
+        x[0] = v >= 0 ? Io::load1(zt + v) : kPad;
+        y[0] = v >= 0 ? Io::load1(zs + v) : kPad;
+        vs_fold8(s, x, y, c);
+        state_vec<T, LPR, kUnroll>(zt + h, zs + h, body, c, li, s);
+        return;
+    }
+    for (int base = 0; base < V; base += kStep * LPR) {
+        float x[8], y[8];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                float x[8], y[8];
-                Io::widen(a[u], x);
-                Io::widen(b[u], y);
-                vs_fold8(s, x, y, c);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int v = base + li + j * LPR;
+            const bool in = v < V;
+            x[j] = in ? Io::load1(zt + v) : kPad;
+            y[j] = in ? Io::load1(zs + v) : kPad;
         }
-        for (; k < nst; k += LPR) {
-            float x[8], y[8];
-            Io::widen(Io::load(zt + (int64_t)k * kStep), x);
-            Io::widen(Io::load(zs + (int64_t)k * kStep), y);
-            vs_fold8(s, x, y, c);
-        }
-    } else {
-        for (int base = 0; base < V; base += kStep * LPR) {
-            float x[8], y[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int v = base + li + j * LPR;
-                const bool in = v < V;
-                x[j] = in ? Io::load1(zt + v) : kPad;
-                y[j] = in ? Io::load1(zs + v) : kPad;
-            }
-            vs_fold8(s, x, y, c);
-        }
+        vs_fold8(s, x, y, c);
     }
 }
 
@@ -353,6 +391,44 @@ __device__ inline GradRow grad_row(const VocabParams &p, int64_t row, float kl, 
     return r;
 }
 
+// Vector steps of the gradient pass over a 16-byte aligned run of n (a
+// multiple of 8) logits and the matching runs of the outputs.
+template <typename T, bool TEACHER, int LPR, int kUnroll>
+__device__ inline void grads_vec(const GradRow &r, float c, const T *zt, const T *zs, T *gs_out, T *gt_out, int n,
+                                 int li) {
+    using Io = VIo<T>;
+    const int nst = n / kStep;
+    int k = li;
+    for (; k + (kUnroll - 1) * LPR < nst; k += kUnroll * LPR) {
+        typename Io::Raw a[kUnroll], b[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            a[u] = Io::load(zt + (int64_t)(k + u * LPR) * kStep);
+            b[u] = Io::load(zs + (int64_t)(k + u * LPR) * kStep);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float x[8], y[8], ds[8], dt[8];
+            Io::widen(a[u], x);
+            Io::widen(b[u], y);
+            grad8<TEACHER>(r, c, x, y, ds, dt);
+            Io::store(gs_out + (int64_t)(k + u * LPR) * kStep, ds);
+            if (TEACHER) Io::store(gt_out + (int64_t)(k + u * LPR) * kStep, dt);
+        }
+    }
+    for (; k < nst; k += LPR) {
+        float x[8], y[8], ds[8], dt[8];
+        Io::widen(Io::load(zt + (int64_t)k * kStep), x);
+        Io::widen(Io::load(zs + (int64_t)k * kStep), y);
+        grad8<TEACHER>(r, c, x, y, ds, dt);
+        Io::store(gs_out + (int64_t)k * kStep, ds);
+        if (TEACHER) Io::store(gt_out + (int64_t)k * kStep, dt);
+    }
+}
+
+// Gradient pass of one row, with the same three layouts as row_state (the
+// head/body/tail split also needs the output rows to start equally far from a
+// 16-byte boundary).
 template <typename T, bool VEC, bool TEACHER, int LPR, int kUnroll = unroll_grad<T>()>
 __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRow &r, int li) {
     using Io = VIo<T>;
@@ -362,51 +438,45 @@ __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRo
     T *gt_out = TEACHER ? static_cast<T *>(p.dzt) + row * (int64_t)p.V : nullptr;
     const int V = p.V;
     if (VEC) {
-        const int nst = V / kStep;
-        int k = li;
-        for (; k + (kUnroll - 1) * LPR < nst; k += kUnroll * LPR) {
-            typename Io::Raw a[kUnroll], b[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                a[u] = Io::load(zt + (int64_t)(k + u * LPR) * kStep);
-                b[u] = Io::load(zs + (int64_t)(k + u * LPR) * kStep);
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                float x[8], y[8], ds[8], dt[8];
-                Io::widen(a[u], x);
-                Io::widen(b[u], y);
-                grad8<TEACHER>(r, p.c, x, y, ds, dt);
-                Io::store(gs_out + (int64_t)(k + u * LPR) * kStep, ds);
-                if (TEACHER) Io::store(gt_out + (int64_t)(k + u * LPR) * kStep, dt);
-            }
-        }
-        for (; k < nst; k += LPR) {
-            float x[8], y[8], ds[8], dt[8];
-            Io::widen(Io::load(zt + (int64_t)k * kStep), x);
-            Io::widen(Io::load(zs + (int64_t)k * kStep), y);
-            grad8<TEACHER>(r, p.c, x, y, ds, dt);
-            Io::store(gs_out + (int64_t)k * kStep, ds);
-            if (TEACHER) Io::store(gt_out + (int64_t)k * kStep, dt);
-        }
-    } else {
-        for (int base = 0; base < V; base += kStep * LPR) {
+        grads_vec<T, TEACHER, LPR, kUnroll>(r, p.c, zt, zs, gs_out, gt_out, V, li);
+        return;
+    }
+    const int h = head_elems(zt);
+    if (h == head_elems(zs) && h == head_elems(gs_out) && (!TEACHER || h == head_elems(gt_out)) && h <= V) {
+        const int body = ((V - h) / kStep) * kStep;
+        int v = -1;
+        if (li < 8) v = li < h ? li : -1;
+        else if (li < 16) v = h + body + (li - 8) < V ? h + body + (li - 8) : -1;
+        if (v >= 0) {
             float x[8], y[8], ds[8], dt[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int v = base + li + j * LPR;
-                const bool in = v < V;
-                x[j] = in ? Io::load1(zt + v) : 0.f;
-                y[j] = in ? Io::load1(zs + v) : 0.f;
-            }
+            for (int j = 0; j < 8; ++j) x[j] = y[j] = 0.f;
+            x[0] = Io::load1(zt + v);
+            y[0] = Io::load1(zs + v);
             grad8<TEACHER>(r, p.c, x, y, ds, dt);
+            Io::store1(gs_out + v, ds[0]);
+            if (TEACHER) Io::store1(gt_out + v, dt[0]);
+        }
+        grads_vec<T, TEACHER, LPR, kUnroll>(r, p.c, zt + h, zs + h, gs_out + h, TEACHER ? gt_out + h : nullptr, body,
+                                            li);
+        return;
+    }
+    for (int base = 0; base < V; base += kStep * LPR) {
+        float x[8], y[8], ds[8], dt[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int v = base + li + j * LPR;
-                if (v < V) {
-                    Io::store1(gs_out + v, ds[j]);
-                    if (TEACHER) Io::store1(gt_out + v, dt[j]);
-                }
+        for (int j = 0; j < 8; ++j) {
+            const int v = base + li + j * LPR;
+            const bool in = v < V;
+            x[j] = in ? Io::load1(zt + v) : 0.f;
+            y[j] = in ? Io::load1(zs + v) : 0.f;
+        }
+        grad8<TEACHER>(r, p.c, x, y, ds, dt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int v = base + li + j * LPR;
+            if (v < V) {
+                Io::store1(gs_out + v, ds[j]);
+                if (TEACHER) Io::store1(gt_out + v, dt[j]);
             }
         }
     }

@@ -172,6 +172,7 @@ VOCAB_WORKLOADS = {
     "kd_logits_odd_f32": VocabWorkload("kd_logits_odd_f32", 9, 50257, "f32", 1.0, "lm", 0.5, 32),
     "kd_logits_short": VocabWorkload("kd_logits_short", 70, 1000, "bf16", 4.0, "iid", 0.0, 33),
     "kd_logits_4k_128k": VocabWorkload("kd_logits_4k_128k", 4096, 128256, "bf16", 2.0, "lm", 0.5, 34),
+    "kd_logits_8k_50257": VocabWorkload("kd_logits_8k_50257", 8192, 50257, "bf16", 2.0, "lm", 0.5, 35),
 }
 
 
