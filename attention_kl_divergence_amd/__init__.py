@@ -75,11 +75,13 @@ def load_library():
     lib.streamkl_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, lay, f, f, i, vp, vp, vp, vp, vp]
     lib.streamkl_fwd_ex.restype = i
     lib.streamkl_bwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, lay, f, f, i, vp, vp, vp, f, vp, vp,
-                                    vp]
+                                    vp, ctypes.c_size_t, vp]
     lib.streamkl_bwd_ex.restype = i
     lib.streamkl_bwd_teacher_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, lay, f, f, i, vp, vp, vp, vp,
-                                            f, vp, vp, vp]
+                                            f, vp, vp, vp, ctypes.c_size_t, vp]
     lib.streamkl_bwd_teacher_ex.restype = i
+    lib.streamkl_bwd_ex_workspace_size.argtypes = [i, i, i, i, i, i, lay, i]
+    lib.streamkl_bwd_ex_workspace_size.restype = ctypes.c_size_t
     i64 = ctypes.c_int64
     lib.streamkl_vocab_fwd.argtypes = [vp, vp, i, i64, i, i64, i64, f, vp, vp, vp, vp, vp]
     lib.streamkl_vocab_fwd.restype = i
@@ -298,11 +300,14 @@ def streamkl_bwd(q_t, k_t, q_s, k_s, lse_t, lse_s, grad_rows=None, grad_scalar=1
     dk = torch.empty((B, heads[3], n_k, d_s), dtype=q_s.dtype, device=dev)
     lay, _keep = _layout(B, H, heads, seqlen_q, seqlen_k, dev)
     if lay is not None:
+        wsb = int(lib.streamkl_bwd_ex_workspace_size(B, H, n_q, n_k, d_t, d_s, ctypes.byref(lay), 0))
+        ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
         code = lib.streamkl_bwd_ex(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
                                    B, H, n_q, n_k, d_t, d_s, strides, ctypes.byref(lay), tau_t, tau_s,
                                    int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr(),
                                    grad_rows.data_ptr() if grad_rows is not None else None, float(grad_scalar),
-                                   dq.data_ptr(), dk.data_ptr(), _stream_ptr(dev))
+                                   dq.data_ptr(), dk.data_ptr(), ws.data_ptr() if ws is not None else None, wsb,
+                                   _stream_ptr(dev))
         _check("streamkl_bwd_ex", code)
         return dq, dk
     code = lib.streamkl_bwd(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t),
@@ -335,12 +340,15 @@ def streamkl_bwd_teacher(q_t, k_t, q_s, k_s, lse_t, lse_s, kl_rows, grad_rows=No
     dk = torch.empty((B, heads[1], n_k, d_t), dtype=q_t.dtype, device=dev)
     lay, _keep = _layout(B, H, heads, seqlen_q, seqlen_k, dev)
     if lay is not None:
+        wsb = int(lib.streamkl_bwd_ex_workspace_size(B, H, n_q, n_k, d_t, d_s, ctypes.byref(lay), 1))
+        ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
         code = lib.streamkl_bwd_teacher_ex(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),
                                            _dtype_code(q_t), B, H, n_q, n_k, d_t, d_s, strides, ctypes.byref(lay),
                                            tau_t, tau_s, int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr(),
                                            kl_rows.data_ptr(),
                                            grad_rows.data_ptr() if grad_rows is not None else None,
-                                           float(grad_scalar), dq.data_ptr(), dk.data_ptr(), _stream_ptr(dev))
+                                           float(grad_scalar), dq.data_ptr(), dk.data_ptr(),
+                                           ws.data_ptr() if ws is not None else None, wsb, _stream_ptr(dev))
         _check("streamkl_bwd_teacher_ex", code)
         return dq, dk
     code = lib.streamkl_bwd_teacher(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),

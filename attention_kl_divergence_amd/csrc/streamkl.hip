@@ -566,6 +566,11 @@ struct BwdParams {
     // output has Hout heads, output head o sums KL heads [o group, (o + 1) group)
     int g_xt, g_xs, g_yt, g_ys, Hout, group;
     const int *len_q, *len_k;  // per-batch valid lengths (null: n_q, n_k)
+    // a group split over nsplit blocks of hsplit KL heads each, which write
+    // fp32 partial gradients [nsplit][B Hout][n_x][DG] to `partial` (a later
+    // launch sums them); n_xblk then counts n_x blocks times nsplit
+    int nsplit, hsplit;
+    float *partial;
 };
 
 // Range [ystart, yend) of streamed rows that stationary block xb meets: all of
@@ -752,7 +757,7 @@ constexpr int kBwdRows = kBwdSub * kBN;
 // FIRST: gradients with respect to the first (teacher) distribution, contracted
 // with the teacher tiles (output width d_t) instead of the student ones.
 template <typename T, int DT, int DS, bool CAUSAL, bool DKMODE, bool GS, bool FIRST, bool GRP>
-__device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams &p, int xb, int bh, char *smem,
+__device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams &p, int xb, int sp, int bh, char *smem,
                                                                 float (*rowv)[3][kBwdRows]) {
     using TileT = Tile<T, DT>;
     using TileS = Tile<T, DS>;
@@ -966,8 +971,9 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     // GRP: several KL heads feed this output head (a separate instantiation,
     // so that the single-head kernels keep their register allocation)
     const int ngroup = GRP ? p.group : 1;
-    for (int u = 0; u < ngroup; ++u) {
-        begin_head(ho * ngroup + u, u == 0);
+    const int u0 = GRP ? sp * p.hsplit : 0, u1 = GRP ? min(ngroup, u0 + p.hsplit) : 1;
+    for (int u = u0; u < u1; ++u) {
+        begin_head(ho * ngroup + u, u == u0);
         for (int st = 0; st < s_lo; ++st) stage_body(st, std::false_type{}, st & 1);
         {
             // plain stages two at a time, so that the ring slot, and with it
@@ -991,7 +997,19 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
 #pragma unroll
         for (int t = 0; t < DG / kTile; ++t) G[t] = f32x16{};
     }
-    if (x < p.n_x) {
+    if (GRP && p.partial && x < p.n_x) {
+        // this split's share of the group: fp32 partial sums
+        float *prow = p.partial + (((int64_t)sp * p.nheads + bh) * p.n_x + x) * DG;
+#pragma unroll
+        for (int t = 0; t < DG / kTile; ++t) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int d0 = t * kTile + grp * 8 + hf * 4;
+                f32x4 o = {G[t][grp * 4 + 0], G[t][grp * 4 + 1], G[t][grp * 4 + 2], G[t][grp * 4 + 3]};
+                *reinterpret_cast<f32x4 *>(prow + d0) = o;
+            }
+        }
+    } else if (x < p.n_x) {
         T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.Hout + ho) * p.n_x + x) * DG;
 #pragma unroll
         for (int t = 0; t < DG / kTile; ++t) {
@@ -1044,9 +1062,33 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
         else hi = mid;
     }
     const bool dk = !(r - lo >= nk || (lo < nq && a_first(lo, r - lo)));
-    const int idx = dk ? r - lo : nq - 1 - lo;
-    if (dk) bwd_block<T, DT, DS, CAUSAL, true, GS, FIRST, GRP>(pk, idx, bh, smem, rowv);
-    else bwd_block<T, DT, DS, CAUSAL, false, GS, FIRST, GRP>(pq, idx, bh, smem, rowv);
+    int idx = dk ? r - lo : nq - 1 - lo, sp = 0;
+    if (GRP) {
+        // split groups: consecutive work items are the splits of one block
+        const int ns = dk ? pk.nsplit : pq.nsplit;
+        sp = idx % ns;
+        idx /= ns;
+    }
+    if (dk) bwd_block<T, DT, DS, CAUSAL, true, GS, FIRST, GRP>(pk, idx, sp, bh, smem, rowv);
+    else bwd_block<T, DT, DS, CAUSAL, false, GS, FIRST, GRP>(pq, idx, sp, bh, smem, rowv);
+}
+
+// Sum of nsplit fp32 partial gradients [nsplit][n] into the output [n] in the
+// input dtype, in a fixed order (n is a multiple of 4).
+template <typename T>
+__global__ __launch_bounds__(256) void streamkl_split_reduce_kernel(const float *partial, int nsplit, int64_t n,
+                                                                    T *out) {
+    const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += stride) {
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(partial + i);
+        for (int j = 1; j < nsplit; ++j) acc += *reinterpret_cast<const f32x4 *>(partial + (int64_t)j * n + i);
+        if constexpr (sizeof(T) == 2) {
+            bf16x4 o = {(bf16_t)acc[0], (bf16_t)acc[1], (bf16_t)acc[2], (bf16_t)acc[3]};
+            *reinterpret_cast<bf16x4 *>(out + i) = o;
+        } else {
+            *reinterpret_cast<f32x4 *>(out + i) = acc;
+        }
+    }
 }
 
 // ================================================================= host side
@@ -1245,6 +1287,21 @@ streamkl_status fwd_common(const void *q_t, const void *k_t, const void *q_s, co
     return STREAMKL_OK;
 }
 
+// Splits of a head group of `group` KL heads whose output kind has `blocks`
+// blocks: enough to give the launch about 1024 work items, each split a run of
+// hsplit KL heads (every split non-empty).
+void group_split(int64_t blocks, int group, int &nsplit, int &hsplit) {
+    nsplit = 1;
+    hsplit = group;
+    if (group <= 1 || blocks >= 1024) return;
+    const int want = (int)std::min<int64_t>(group, (1024 + blocks - 1) / blocks);
+    hsplit = (group + want - 1) / want;
+    nsplit = (group + hsplit - 1) / hsplit;
+}
+size_t split_bytes(int nsplit, int64_t nheads_out, int n_x, int dg) {
+    return (size_t)nsplit * nheads_out * n_x * dg * sizeof(float);
+}
+
 // Both backward entry points: gradients of sum_r g_r KL_r with respect to the
 // student (first = false, outputs d_s wide) or the teacher (first = true,
 // outputs d_t wide, needs the forward's per-row KL).  Without grouped heads
@@ -1256,9 +1313,11 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
                            streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
                            const int64_t *strides, const streamkl_layout *lay, float tau_t, float tau_s, int causal,
                            const float *lse_t, const float *lse_s, const float *kl_rows, const float *grad_rows,
-                           float grad_scalar, void *dq_out, void *dk_out, bool first, void *stream) {
+                           float grad_scalar, void *dq_out, void *dk_out, bool first, void *workspace,
+                           size_t workspace_bytes, void *stream) {
     const Shape s{B, H, n_q, n_k, d_t, d_s};
     if (B < 1 || H < 1) return STREAMKL_ERR_INVALID;
+    if (workspace && ((uintptr_t)workspace) % 16 != 0) return STREAMKL_ERR_INVALID;
     Heads hd;
     streamkl_status rc = resolve_layout(lay, H, hd);
     if (rc != STREAMKL_OK) return rc;
@@ -1300,6 +1359,9 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
         p.lse_t = lse_t; p.lse_s = lse_s; p.g = grad_rows; p.g_scalar = grad_scalar;
         p.kl = kl_rows;
         p.out = dk ? dk_out : dq_out;
+        p.nsplit = 1;
+        p.hsplit = p.group;
+        p.partial = nullptr;
     }
     const bool gs = grad_rows == nullptr;
     const bool grp = pp[0].group > 1 || pp[1].group > 1;
@@ -1327,15 +1389,56 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
         return STREAMKL_OK;
     }
     for (int pass = 0; pass < 2; ++pass) {
+        BwdParams &cur = pp[pass];
+        // long groups over few output blocks: split each group over several
+        // blocks when the caller gave room for their partial sums
+        const int dg = first ? d_t : d_s;
+        int ns = 1, hs_ = cur.group;
+        group_split(cur.nheads * cur.n_xblk, cur.group, ns, hs_);
+        if (ns > 1 && split_bytes(ns, cur.nheads, cur.n_x, dg) <= workspace_bytes && workspace) {
+            cur.nsplit = ns;
+            cur.hsplit = hs_;
+            cur.partial = static_cast<float *>(workspace);
+            cur.n_xblk *= ns;
+        }
         BwdParams none = pp[1 - pass];
         none.n_xblk = 0;
-        none.nheads = pp[pass].nheads;
-        pp[pass].rank_major = none.rank_major = order(pass == 0, pass == 1, pp[pass].nheads);
-        if (pass == 0) fn(pp[0], none, pp[0].nheads * pp[0].n_xblk, hs);
-        else fn(none, pp[1], pp[1].nheads * pp[1].n_xblk, hs);
+        none.nheads = cur.nheads;
+        cur.rank_major = none.rank_major = order(pass == 0, pass == 1, cur.nheads);
+        if (pass == 0) fn(cur, none, cur.nheads * cur.n_xblk, hs);
+        else fn(none, cur, cur.nheads * cur.n_xblk, hs);
         if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+        if (cur.nsplit > 1) {
+            const int64_t n = (int64_t)cur.nheads * cur.n_x * dg;
+            const unsigned grid = (unsigned)std::min<int64_t>((n / 4 + 255) / 256, 4096);
+            if (bf)
+                hipLaunchKernelGGL(streamkl_split_reduce_kernel<bf16_t>, dim3(grid), dim3(256), 0, hs, cur.partial,
+                                   cur.nsplit, n, static_cast<bf16_t *>(cur.out));
+            else
+                hipLaunchKernelGGL(streamkl_split_reduce_kernel<float>, dim3(grid), dim3(256), 0, hs, cur.partial,
+                                   cur.nsplit, n, static_cast<float *>(cur.out));
+            if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
+        }
     }
     return STREAMKL_OK;
+}
+
+// Workspace bytes of a grouped backward (0 when no group is split).
+size_t bwd_ex_workspace(int B, int H, int n_q, int n_k, int d_t, int d_s, const streamkl_layout *lay, bool first) {
+    if (B < 1 || H < 1 || n_q < 1 || n_k < 1) return 0;
+    Heads hd;
+    if (resolve_layout(lay, H, hd) != STREAMKL_OK) return 0;
+    size_t need = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool dk = pass == 1;
+        const int hout = first ? hd.h[dk ? 1 : 0] : hd.h[dk ? 3 : 2];
+        const int group = H / hout, n_x = dk ? n_k : n_q;
+        const int nblk = B * hout * ((n_x + kBlockX - 1) / kBlockX);
+        int ns = 1, hsp = group;
+        group_split(nblk, group, ns, hsp);
+        if (ns > 1) need = std::max(need, split_bytes(ns, B * hout, n_x, first ? d_t : d_s));
+    }
+    return need;
 }
 
 }  // namespace
@@ -1445,7 +1548,7 @@ streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, 
                              const float *lse_s, const float *grad_rows, float grad_scalar, void *dq_s,
                              void *dk_s, void *stream) {
     return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s, causal,
-                      lse_t, lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, stream);
+                      lse_t, lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, nullptr, 0, stream);
 }
 
 streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
@@ -1455,7 +1558,7 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
                                      const float *grad_rows, float grad_scalar, void *dq_t, void *dk_t,
                                      void *stream) {
     return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s, causal,
-                      lse_t, lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, stream);
+                      lse_t, lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, nullptr, 0, stream);
 }
 
 streamkl_status streamkl_fwd_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
@@ -1468,13 +1571,20 @@ streamkl_status streamkl_fwd_ex(const void *q_t, const void *k_t, const void *q_
                       n_k, 1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
 }
 
+size_t streamkl_bwd_ex_workspace_size(int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                      const streamkl_layout *layout, int first) {
+    return bwd_ex_workspace(B, H, n_q, n_k, d_t, d_s, layout, first != 0);
+}
+
 streamkl_status streamkl_bwd_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
                                 streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
                                 const int64_t *strides, const streamkl_layout *layout, float tau_t, float tau_s,
                                 int causal, const float *lse_t, const float *lse_s, const float *grad_rows,
-                                float grad_scalar, void *dq_s, void *dk_s, void *stream) {
+                                float grad_scalar, void *dq_s, void *dk_s, void *workspace, size_t workspace_bytes,
+                                void *stream) {
     return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, layout, tau_t, tau_s, causal,
-                      lse_t, lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, stream);
+                      lse_t, lse_s, nullptr, grad_rows, grad_scalar, dq_s, dk_s, false, workspace, workspace_bytes,
+                      stream);
 }
 
 streamkl_status streamkl_bwd_teacher_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
@@ -1482,9 +1592,10 @@ streamkl_status streamkl_bwd_teacher_ex(const void *q_t, const void *k_t, const 
                                         const int64_t *strides, const streamkl_layout *layout, float tau_t,
                                         float tau_s, int causal, const float *lse_t, const float *lse_s,
                                         const float *kl_rows, const float *grad_rows, float grad_scalar, void *dq_t,
-                                        void *dk_t, void *stream) {
+                                        void *dk_t, void *workspace, size_t workspace_bytes, void *stream) {
     return bwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, layout, tau_t, tau_s, causal,
-                      lse_t, lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, stream);
+                      lse_t, lse_s, kl_rows, grad_rows, grad_scalar, dq_t, dk_t, true, workspace, workspace_bytes,
+                      stream);
 }
 
 }  // extern "C"

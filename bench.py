@@ -483,10 +483,14 @@ def main():
             if rc:
                 raise RuntimeError(skl.status_string(rc))
 
+        wsb = int(lib.streamkl_bwd_ex_workspace_size(B, H, w.n_q, w.n_k, w.d_t, w.d_s, ctypes.byref(lay), 0))
+        wsg = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+
         def bwd_g():
             rc = lib.streamkl_bwd_ex(ptr["q_t"], ptr["k_t"], ptr["q_s"], ks_g.data_ptr(), code, B, H, w.n_q, w.n_k,
                                      w.d_t, w.d_s, None, ctypes.byref(lay), w.tau_t, w.tau_s, int(w.causal),
-                                     lt.data_ptr(), ls.data_ptr(), None, 1.0, dq.data_ptr(), dkg.data_ptr(), sp)
+                                     lt.data_ptr(), ls.data_ptr(), None, 1.0, dq.data_ptr(), dkg.data_ptr(),
+                                     wsg.data_ptr() if wsb else None, wsb, sp)
             if rc:
                 raise RuntimeError(skl.status_string(rc))
         for _ in range(args.warmup):
@@ -502,7 +506,7 @@ def main():
         torch.cuda.synchronize()
         g_f = np.array([e[0].elapsed_time(e[1]) for e in gev])
         g_b = np.array([e[1].elapsed_time(e[2]) for e in gev])
-        res["grouped"] = {"student_kv_heads": nkv, "fwd_ms": round(float(np.mean(g_f)), 4),
+        res["grouped"] = {"student_kv_heads": nkv, "workspace_bytes": wsb, "fwd_ms": round(float(np.mean(g_f)), 4),
                           "bwd_ms": round(float(np.mean(g_b)), 4),
                           "fwd_tflops": round(F / (np.mean(g_f) * 1e-3) / 1e12, 2),
                           "bwd_tflops": round(Bw / (np.mean(g_b) * 1e-3) / 1e12, 2)}

@@ -243,20 +243,34 @@ streamkl_status streamkl_fwd_ex(const void *q_t, const void *k_t, const void *q_
                                 int causal, float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
                                 void *stream);
 
-/* streamkl_bwd with a layout: dq_s, dk_s in the student's head counts. */
+/* Workspace bytes that streamkl_bwd_ex (first = 0) or streamkl_bwd_teacher_ex
+ * (first = 1) can use for this shape and layout; 0 when none helps.  A
+ * gradient block of a shared head loops over the KL heads that read it; when
+ * such blocks are few (for instance one key head shared by every query head)
+ * each group is split over several blocks that write fp32 partial sums here,
+ * summed afterwards in a fixed order. */
+size_t streamkl_bwd_ex_workspace_size(int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                      const streamkl_layout *layout, int first);
+
+/* streamkl_bwd with a layout: dq_s, dk_s in the student's head counts.
+ * workspace: device, 16-byte aligned, or NULL; with at least
+ * streamkl_bwd_ex_workspace_size bytes long head groups are split (same
+ * results up to rounding), otherwise they are not (no error). */
 streamkl_status streamkl_bwd_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
                                 streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
                                 const int64_t *strides, const streamkl_layout *layout, float tau_t, float tau_s,
                                 int causal, const float *lse_t, const float *lse_s, const float *grad_rows,
-                                float grad_scalar, void *dq_s, void *dk_s, void *stream);
+                                float grad_scalar, void *dq_s, void *dk_s, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
-/* streamkl_bwd_teacher with a layout: dq_t, dk_t in the teacher's head counts. */
+/* streamkl_bwd_teacher with a layout: dq_t, dk_t in the teacher's head
+ * counts; workspace as for streamkl_bwd_ex. */
 streamkl_status streamkl_bwd_teacher_ex(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
                                         streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
                                         const int64_t *strides, const streamkl_layout *layout, float tau_t,
                                         float tau_s, int causal, const float *lse_t, const float *lse_s,
                                         const float *kl_rows, const float *grad_rows, float grad_scalar, void *dq_t,
-                                        void *dk_t, void *stream);
+                                        void *dk_t, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Vocabulary-logit KL at temperature.  The distillation loss of "Lecture 05 -

@@ -237,11 +237,26 @@ def test_layout_entry_points_reject_bad_layouts_before_any_hip_call():
         if first:
             return lib.streamkl_bwd_teacher_ex(A, A + 0x100000, A + 0x200000, A + 0x300000, skl.STREAMKL_BF16, 2, 8,
                                                100, 300, 128, 64, None, ctypes.byref(lay), 0.088, 0.125, 0, A, A,
-                                               kw.get("kl", A), None, 1.0, A + 0x700000, A + 0x800000, None)
+                                               kw.get("kl", A), None, 1.0, A + 0x700000, A + 0x800000, None, 0, None)
         return lib.streamkl_bwd_ex(A, A + 0x100000, A + 0x200000, A + 0x300000, skl.STREAMKL_BF16, 2, 8, 100, 300,
                                    128, 64, None, ctypes.byref(lay), 0.088, 0.125, 0, A, A, None, 1.0,
-                                   kw.get("dq", A + 0x700000), A + 0x800000, None)
+                                   kw.get("dq", A + 0x700000), A + 0x800000, kw.get("ws", None), 1 << 30, None)
     assert bwd(False, hk_s=5) == INV
     assert bwd(False, hk_s=2, dq=None) == INV
     assert bwd(True, hk_t=2, kl=None) == INV
     assert bwd(True, hq_t=16) == INV    # 16 does not divide H = 8
+    assert bwd(False, hk_s=2, ws=A + 8) == INV   # misaligned workspace
+    # workspace sizes: none for single heads or plentiful blocks, partial sums for a long group over few blocks
+    one = skl.StreamKLLayout(0, 0, 0, 1, None, None)
+    four = skl.StreamKLLayout(0, 0, 0, 4, None, None)
+    assert lib.streamkl_bwd_ex_workspace_size(2, 16, 16384, 16384, 128, 128, None, 0) == 0
+    # groups of 4 over 2 x 4 x 128 key blocks: already 1024 work items, no split
+    assert lib.streamkl_bwd_ex_workspace_size(2, 16, 16384, 16384, 128, 128, ctypes.byref(four), 0) == 0
+    # one key head: 2 x 128 key blocks, groups of 16 split 4 ways: 4 partial dK_s tensors in fp32
+    n16 = lib.streamkl_bwd_ex_workspace_size(2, 16, 16384, 16384, 128, 128, ctypes.byref(one), 0)
+    assert n16 == 4 * 2 * 1 * 16384 * 128 * 4
+    # 2 x 32 key blocks at 4K: split 16 ways
+    n4 = lib.streamkl_bwd_ex_workspace_size(2, 16, 4096, 4096, 128, 128, ctypes.byref(one), 0)
+    assert n4 == 16 * 2 * 1 * 4096 * 128 * 4
+    # the teacher's heads decide the teacher gradients' split: none here
+    assert lib.streamkl_bwd_ex_workspace_size(2, 16, 4096, 4096, 128, 128, ctypes.byref(one), 1) == 0

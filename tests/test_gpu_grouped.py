@@ -170,3 +170,53 @@ def test_grouped_autograd():
     check_grad(d["q_s"].grad.cpu().numpy(), ref["dq_s"], "f32", "autograd dq_s")
     check_grad(d["k_s"].grad.cpu().numpy(), ref["dk_s"], "f32", "autograd dk_s")
     assert d["k_s"].grad.shape == (B, 2, n_k, 64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_groups_equal_unsplit_and_oracle(causal):
+    """One key head shared by all 16 query heads of the student (and of the
+    teacher): the key-major blocks are few, so each head group is split over
+    several blocks writing fp32 partial sums to the workspace.  The split and
+    unsplit launches agree to rounding, and both match the oracle, for
+    student and teacher gradients with per-row weights of both signs."""
+    import ctypes
+    B, H, n = 1, 16, 256
+    heads = (H, 1, H, 1)
+    x = _draw(21 + causal, B, heads, n, n, 128, 128, "bf16")
+    g = np.random.default_rng(8).standard_normal((B, H, n)).astype(np.float32)
+    t = float(np.float32(1 / np.sqrt(128)))
+    ref = _reference(x, H, t, t, causal, g=g)
+    d = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    kl, lt, ls, _ = skl.streamkl_fwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], causal=causal)
+    gt = torch.from_numpy(g).cuda()
+    lib = skl.load_library()
+    lay = skl.StreamKLLayout(*heads, None, None)
+    strides = (ctypes.c_int64 * 12)(*[s for k in ("q_t", "k_t", "q_s", "k_s") for s in d[k].stride()[:3]])
+    outs = {}
+    for first in (0, 1):
+        wsb = int(lib.streamkl_bwd_ex_workspace_size(B, H, n, n, 128, 128, ctypes.byref(lay), first))
+        assert wsb > 0
+        ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+        for split in (False, True):
+            dq = torch.empty_like(d["q_t" if first else "q_s"])
+            dk = torch.empty_like(d["k_t" if first else "k_s"])
+            args = [d["q_t"].data_ptr(), d["k_t"].data_ptr(), d["q_s"].data_ptr(), d["k_s"].data_ptr(),
+                    skl.STREAMKL_BF16, B, H, n, n, 128, 128, strides, ctypes.byref(lay), t, t, int(causal),
+                    lt.data_ptr(), ls.data_ptr()]
+            wsp = (ws.data_ptr(), wsb) if split else (None, 0)
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            if first:
+                rc = lib.streamkl_bwd_teacher_ex(*args, kl.data_ptr(), gt.data_ptr(), 1.0, dq.data_ptr(),
+                                                 dk.data_ptr(), *wsp, stream)
+            else:
+                rc = lib.streamkl_bwd_ex(*args, gt.data_ptr(), 1.0, dq.data_ptr(), dk.data_ptr(), *wsp, stream)
+            assert rc == 0, skl.status_string(rc)
+            torch.cuda.synchronize()
+            outs[(first, split)] = (dq.float().cpu().numpy().astype(np.float64),
+                                    dk.float().cpu().numpy().astype(np.float64))
+    for first, (nq_, nk_) in ((0, ("dq_s", "dk_s")), (1, ("dq_t", "dk_t"))):
+        for split in (False, True):
+            check_grad(outs[(first, split)][0], ref[nq_], "bf16", f"{nq_} split={split}")
+            check_grad(outs[(first, split)][1], ref[nk_], "bf16", f"{nk_} split={split}")
+        a, b = outs[(first, False)][1], outs[(first, True)][1]
+        assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a)

@@ -71,7 +71,8 @@ def test_no_spills_in_the_mfma_loops(asm):
     text = "\n".join(asm)
     found = list(re.finditer(r"\.name:\s+(_ZN12_GLOBAL__N_1\d+streamkl_\w+)[\s\S]*?"
                              r"\.private_segment_fixed_size:\s+(\d+)", text))
-    assert len(found) == 98  # 96 forward/backward instantiations + the sum and merge kernels
+    # 96 forward/backward instantiations + the sum, merge and two split-reduce kernels
+    assert len(found) == 100
     for m in found:
         # grouped-head backward kernels (last template flag GRP = 1) keep more
         # state across their head loop and spill at the head boundaries
