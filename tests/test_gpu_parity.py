@@ -11,7 +11,6 @@ same seeded inputs.
 * edge cases: single rows/keys, causal rectangles, identical teacher and
   student, a uniform student, strided views, determinism, NaN confinement.
 """
-import math
 
 import numpy as np
 import pytest
