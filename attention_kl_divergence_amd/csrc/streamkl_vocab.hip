@@ -393,18 +393,21 @@ __device__ inline GradRow grad_row(const VocabParams &p, int64_t row, float kl, 
 
 // Vector steps of the gradient pass over a 16-byte aligned run of n (a
 // multiple of 8) logits and the matching runs of the outputs.
-template <typename T, bool TEACHER, int LPR, int kUnroll>
+// REV: walk the steps from the end of the run (the fused launch's second
+// pass, so that it starts with the logits its first pass read last).
+template <typename T, bool TEACHER, int LPR, int kUnroll, bool REV = false>
 __device__ inline void grads_vec(const GradRow &r, float c, const T *zt, const T *zs, T *gs_out, T *gt_out, int n,
                                  int li) {
     using Io = VIo<T>;
     const int nst = n / kStep;
+    auto at = [&](int k) { return (int64_t)(REV ? nst - 1 - k : k) * kStep; };
     int k = li;
     for (; k + (kUnroll - 1) * LPR < nst; k += kUnroll * LPR) {
         typename Io::Raw a[kUnroll], b[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            a[u] = Io::load(zt + (int64_t)(k + u * LPR) * kStep);
-            b[u] = Io::load(zs + (int64_t)(k + u * LPR) * kStep);
+            a[u] = Io::load(zt + at(k + u * LPR));
+            b[u] = Io::load(zs + at(k + u * LPR));
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -412,24 +415,24 @@ __device__ inline void grads_vec(const GradRow &r, float c, const T *zt, const T
             Io::widen(a[u], x);
             Io::widen(b[u], y);
             grad8<TEACHER>(r, c, x, y, ds, dt);
-            Io::store(gs_out + (int64_t)(k + u * LPR) * kStep, ds);
-            if (TEACHER) Io::store(gt_out + (int64_t)(k + u * LPR) * kStep, dt);
+            Io::store(gs_out + at(k + u * LPR), ds);
+            if (TEACHER) Io::store(gt_out + at(k + u * LPR), dt);
         }
     }
     for (; k < nst; k += LPR) {
         float x[8], y[8], ds[8], dt[8];
-        Io::widen(Io::load(zt + (int64_t)k * kStep), x);
-        Io::widen(Io::load(zs + (int64_t)k * kStep), y);
+        Io::widen(Io::load(zt + at(k)), x);
+        Io::widen(Io::load(zs + at(k)), y);
         grad8<TEACHER>(r, c, x, y, ds, dt);
-        Io::store(gs_out + (int64_t)k * kStep, ds);
-        if (TEACHER) Io::store(gt_out + (int64_t)k * kStep, dt);
+        Io::store(gs_out + at(k), ds);
+        if (TEACHER) Io::store(gt_out + at(k), dt);
     }
 }
 
 // Gradient pass of one row, with the same three layouts as row_state (the
 // head/body/tail split also needs the output rows to start equally far from a
 // 16-byte boundary).
-template <typename T, bool VEC, bool TEACHER, int LPR, int kUnroll = unroll_grad<T>()>
+template <typename T, bool VEC, bool TEACHER, int LPR, int kUnroll = unroll_grad<T>(), bool REV = false>
 __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRow &r, int li) {
     using Io = VIo<T>;
     const T *zt = static_cast<const T *>(p.zt) + row * p.ld_t;
@@ -438,7 +441,7 @@ __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRo
     T *gt_out = TEACHER ? static_cast<T *>(p.dzt) + row * (int64_t)p.V : nullptr;
     const int V = p.V;
     if (VEC) {
-        grads_vec<T, TEACHER, LPR, kUnroll>(r, p.c, zt, zs, gs_out, gt_out, V, li);
+        grads_vec<T, TEACHER, LPR, kUnroll, REV>(r, p.c, zt, zs, gs_out, gt_out, V, li);
         return;
     }
     const int h = head_elems(zt);
@@ -457,8 +460,8 @@ __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRo
             Io::store1(gs_out + v, ds[0]);
             if (TEACHER) Io::store1(gt_out + v, dt[0]);
         }
-        grads_vec<T, TEACHER, LPR, kUnroll>(r, p.c, zt + h, zs + h, gs_out + h, TEACHER ? gt_out + h : nullptr, body,
-                                            li);
+        grads_vec<T, TEACHER, LPR, kUnroll, REV>(r, p.c, zt + h, zs + h, gs_out + h, TEACHER ? gt_out + h : nullptr,
+                                                 body, li);
         return;
     }
     for (int base = 0; base < V; base += kStep * LPR) {
@@ -517,7 +520,8 @@ __global__ __launch_bounds__(block_threads<WPR>()) void streamkl_vocab_fused_ker
         p.lse_s[row] = r.ls;
     }
     const GradRow gr = grad_row<TEACHER>(p, row, r.kl, r.lt, r.ls);
-    row_grads<T, VEC, TEACHER, LPR, kUnrollState>(p, row, gr, li);
+    // second pass from the end of the row: the logits read last are the likeliest still cached
+    row_grads<T, VEC, TEACHER, LPR, kUnrollState, true>(p, row, gr, li);
 }
 
 // ================================================================= host side
