@@ -220,3 +220,65 @@ def test_split_groups_equal_unsplit_and_oracle(causal):
             check_grad(outs[(first, split)][1], ref[nk_], "bf16", f"{nk_} split={split}")
         a, b = outs[(first, False)][1], outs[(first, True)][1]
         assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a)
+
+
+def _identities_grouped(xo, dq, dk, hq, hk):
+    """At any size: sum_j dK_s[j] = 0 per key head, and per key head the sum
+    over its query heads of <Q_s, dQ_s> equals <K_s, dK_s>."""
+    B = dq.shape[0]
+    g = hq // hk
+    for b in range(B):
+        for j in range(hk):
+            nrm = np.linalg.norm(dk[b, j])
+            assert np.linalg.norm(dk[b, j].sum(axis=0)) <= 1e-2 * nrm + 1e-12
+            lhs = sum(float(np.sum(xo["q_s"][b, h] * dq[b, h])) for h in range(j * g, (j + 1) * g))
+            rhs = float(np.sum(xo["k_s"][b, j] * dk[b, j]))
+            scale = sum(np.linalg.norm(xo["q_s"][b, h]) * np.linalg.norm(dq[b, h]) for h in range(j * g, (j + 1) * g))
+            scale += np.linalg.norm(xo["k_s"][b, j]) * nrm
+            assert abs(lhs - rhs) <= 1e-2 * scale
+
+
+@pytest.mark.parametrize("name,kv,resize", [
+    ("corr_16k", 4, None),                                   # the benchmark's --student-kv-heads 4 launch
+    ("corr_4k", 1, dict(B=1, n_q=2048, n_k=2048, seed=77)),  # one shared key head: split groups
+])
+def test_grouped_full_size_sampled(name, kv, resize):
+    """Student keys shared by groups of query heads at the measured sizes:
+    sampled KL rows and dQ_s rows (and, for the smaller shape, sampled dK_s
+    keys summed over their KL heads) against the oracle on the expanded heads,
+    plus the identities that hold at any size."""
+    from attention_kl_divergence_amd import inputs
+    w = inputs.WORKLOADS[name]
+    if resize:
+        w = w.resized(**resize)
+    print(f"[grouped full] {w.name} {w.B}x{w.H}x{w.n_q} with {kv} student key heads", flush=True)
+    x = inputs.make(w)
+    x["k_s"] = np.ascontiguousarray(x["k_s"][:, :kv])
+    d = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    kl, lt, ls, tot = skl.streamkl_fwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"])
+    dq, dk = skl.streamkl_bwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], lt, ls)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    kl, lt, ls, dq, dk = f(kl), f(lt), f(ls), f(dq), f(dk)
+    xo = {k: v.astype(np.float64) for k, v in x.items()}
+    del x, d
+    xe = dict(xo)
+    xe["k_s"] = np.repeat(xo["k_s"], w.H // kv, axis=1)
+    rng = np.random.default_rng(w.seed + 9)
+    n_rows = w.B * w.H * w.n_q
+    rows = np.array(sorted(set(rng.choice(n_rows, 40, replace=False).tolist()) | {0, n_rows - 1}), dtype=np.int64)
+    rkl, rlt, rls = oracle.fwd_rows(xe["q_t"], xe["k_t"], xe["q_s"], xe["k_s"], w.tau_t, w.tau_s, False, rows)
+    check_kl(kl.ravel()[rows], rkl, "bf16", "grouped full kl")
+    check_lse(lt.ravel()[rows], rlt, "bf16", "grouped full lse_t")
+    check_lse(ls.ravel()[rows], rls, "bf16", "grouped full lse_s")
+    qrows = rows[::3]
+    rdq = oracle.dq_rows(xe["q_t"], xe["k_t"], xe["q_s"], xe["k_s"], w.tau_t, w.tau_s, False, qrows)
+    check_grad(dq.reshape(-1, w.d_s)[qrows], rdq, "bf16", "grouped full dq_s rows")
+    if resize:
+        keys = np.array(sorted(set(rng.choice(w.n_k, 6, replace=False).tolist()) | {0, w.n_k - 1}), dtype=np.int64)
+        b = w.B - 1
+        rdk = sum(oracle.dk_keys(xe["q_t"], xe["k_t"], xe["q_s"], xe["k_s"], w.tau_t, w.tau_s, False, b, h, keys)
+                  for h in range(w.H))
+        check_grad(dk[b, 0][keys], rdk, "bf16", "grouped full dk_s keys (summed over the group)")
+    assert abs(float(tot.item()) - float(np.sum(kl))) <= 1e-6 * float(np.sum(np.abs(kl)))
+    _identities_grouped(xo, dq, dk, w.H, kv)
