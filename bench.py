@@ -119,6 +119,26 @@ def committed_traffic(kernel, workload, src="streamkl.hip"):
         return None
 
 
+def committed_sclk(workload):
+    """Average shader clocks (GHz) of the forward and backward kernels from the
+    committed counter summary, if the kernel source is unchanged since."""
+    path = os.path.join(ROOT, "profiles", f"streamkl_fwd_bwd.{workload}.sclk.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["sclk_ghz_fwd"]), float(vals["sclk_ghz_bwd"])
+    except (KeyError, ValueError):
+        return None
+
+
 def copy_calibration(mib, steps):
     """A device-to-device copy of a known number of bytes, for scaling the HBM
     byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
@@ -445,6 +465,16 @@ def main():
                      "traffic": committed_traffic(dom_kernel, w.name),
                      "ms_per_launch": round(float(np.mean(t_f if dominant == "fwd" else t_b)), 4)},
     }
+    clk = committed_sclk(w.name)
+    if clk is not None and w.dtype == "bf16":
+        # the MFMA peak at the clock the kernels actually ran at (256 CUs x 4096 bf16 flop/clk)
+        f_ghz, b_ghz = clk
+        t_f_mean, t_b_mean = float(np.mean(t_f)), float(np.mean(t_b))
+        ghz = (f_ghz * t_f_mean + b_ghz * t_b_mean) / (t_f_mean + t_b_mean)
+        clock_peak = 256 * 4096 * ghz * 1e9 / 1e12
+        res["clock_derived_peak"] = {"sclk_ghz": round(ghz, 3), "peak_tflops": round(clock_peak, 1),
+                                     "pct_peak": round(100.0 * value / clock_peak, 2),
+                                     "source": f"profiles/streamkl_fwd_bwd.{w.name}.sclk.txt"}
     if args.teacher_grads:
         dqt = torch.empty((B, H, w.n_q, w.d_t), dtype=tdt, device=dev)
         dkt = torch.empty((B, H, w.n_k, w.d_t), dtype=tdt, device=dev)
