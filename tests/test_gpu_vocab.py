@@ -213,3 +213,29 @@ def test_vocab_full_size_sampled_rows(full_vocab):
     assert abs(float(tot.item()) - float(np.sum(k))) <= 1e-3 * max(1.0, float(np.sum(np.abs(k))))
     rowsum = fdzs.float().sum(dim=1).abs().max().item()
     assert rowsum <= 1e-5, rowsum
+
+
+def test_vocab_rows_beyond_one_launch():
+    """More rows than one launch covers (2^20): the host splits the rows over
+    consecutive launches; rows on both sides of the boundary match the oracle,
+    and the sum covers every row."""
+    rows, V = (1 << 20) + 37, 16
+    rng = np.random.default_rng(95)
+    zt = _round_bf16_np(rng.standard_normal((rows, V), dtype=np.float32) * 2.0)
+    zs = _round_bf16_np(zt + 0.5 * rng.standard_normal((rows, V), dtype=np.float32))
+    dt, ds = _dev(zt, "bf16"), _dev(zs, "bf16")
+    kl, lt, ls, tot, dzs, _ = skl.streamkl_vocab_fwd_bwd(dt, ds, 1.5, grad_scalar=0.5)
+    torch.cuda.synchronize()
+    pick = np.array([0, 1, (1 << 20) - 2, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, rows - 1], dtype=np.int64)
+    rkl, rlt, _, _ = oracle.vocab_fwd(zt[pick].astype(np.float64), zs[pick].astype(np.float64), 1.5)
+    check_kl(_np(kl)[pick], rkl, "bf16", "many rows kl")
+    check_lse(_np(lt)[pick], rlt, "bf16", "many rows lse_t")
+    rg = oracle.vocab_bwd(zt[pick].astype(np.float64), zs[pick].astype(np.float64), 1.5, g=0.5)
+    check_grad(_np(dzs[torch.from_numpy(pick).cuda()]), rg, "bf16", "many rows dz_s")
+    k = _np(kl)
+    assert abs(float(tot.item()) - float(np.sum(k))) <= 1e-4 * max(1.0, float(np.sum(np.abs(k))))
+
+
+def _round_bf16_np(a):
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)).view(np.float32)
