@@ -260,3 +260,24 @@ def test_full_size_sampled_parity(name):
                 np.linalg.norm(xo["k_s"][b, h]) * nrm
             assert abs(lhs - rhs) <= 1e-2 * scale
     print(f"[full] {name}: ok, mean KL {float(np.mean(out['kl'])):.4f}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sharp_and_rising_scores_force_reference_moves(dtype):
+    """Large score scales (sharp rows) and scores that rise by far more than
+    2^64 in the exponent from one key tile to the next: the forward's lazy
+    reference maxima must move on almost every tile, and the backward's
+    recomputed probabilities must still match the oracle."""
+    w = W["corr_4k"].resized(B=1, H=2, n_q=70, n_k=333, dtype=dtype, seed=230)
+    x = inputs.make(w)
+    _full_compare(w, x, tau_t=1.0, tau_s=0.7)
+    # rising scores: teacher key j is a multiple of the all-ones direction growing with j
+    d = w.d_t
+    ramp = (np.arange(w.n_k, dtype=np.float32) / w.n_k * np.float32(20.0))[None, None, :, None]
+    x2 = dict(x)
+    x2["q_t"] = np.ones_like(x["q_t"])
+    x2["k_t"] = (np.ones((w.B, w.H, w.n_k, d), np.float32) * ramp).astype(np.float32)
+    x2["k_s"] = (x["k_s"] + np.float32(0.5) * x2["k_t"]).astype(np.float32)
+    if dtype == "bf16":
+        x2 = {k: inputs.round_bf16(v) for k, v in x2.items()}
+    _full_compare(w, x2)
