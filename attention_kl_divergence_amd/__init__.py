@@ -30,10 +30,12 @@ _lib = None
 
 
 class StreamKLLayout(ctypes.Structure):
-    """streamkl_layout: head counts of q_t, k_t, q_s, k_s (0 = H) and per-batch
-    valid lengths (device int32 [B] pointers, or None)."""
+    """streamkl_layout: head counts of q_t, k_t, q_s, k_s (0 = H), per-batch
+    valid lengths (device int32 [B] pointers, or None) and packed-sequence
+    offsets (device int32 [B + 1] pointers, or None)."""
     _fields_ = [("heads_q_t", ctypes.c_int), ("heads_k_t", ctypes.c_int), ("heads_q_s", ctypes.c_int),
-                ("heads_k_s", ctypes.c_int), ("seqlen_q", ctypes.c_void_p), ("seqlen_k", ctypes.c_void_p)]
+                ("heads_k_s", ctypes.c_int), ("seqlen_q", ctypes.c_void_p), ("seqlen_k", ctypes.c_void_p),
+                ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p)]
 
 
 class StreamKLError(RuntimeError):
@@ -171,7 +173,7 @@ def _layout(B, H, heads, seqlen_q, seqlen_k, dev):
         t = t.contiguous()
         keep.append(t)
         ptrs.append(t.data_ptr())
-    lay = StreamKLLayout(heads[0], heads[1], heads[2], heads[3], ptrs[0], ptrs[1])
+    lay = StreamKLLayout(heads[0], heads[1], heads[2], heads[3], ptrs[0], ptrs[1], None, None)
     return lay, tuple(keep)
 
 
@@ -466,6 +468,98 @@ def streamkl_vocab_fwd_bwd(z_t, z_s, temperature=1.0, grad_rows=None, grad_scala
     return kl, lt, ls, tot, dzs.view(shape), (dzt.view(shape) if dzt is not None else None)
 
 
+def _inputs_varlen(q_t, k_t, q_s, k_s, cu_q, cu_k, max_q, max_k):
+    """Check packed [rows, heads, d] tensors and their int32 [B + 1] offsets;
+    returns ((B, H, n_q, n_k, d_t, d_s), strides, heads)."""
+    import torch
+    ts = (q_t, k_t, q_s, k_s)
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise ValueError("packed q_t, k_t, q_s, k_s must be 3-D tensors [rows, heads, d]")
+        if t.device.type != "cuda" or t.stride(-1) != 1:
+            raise ValueError("inputs must be device (HIP) tensors with a contiguous last dimension")
+    if len({t.dtype for t in ts}) != 1 or len({t.device for t in ts}) != 1:
+        raise ValueError("inputs must share dtype and device")
+    for name, c in (("cu_seqlens_q", cu_q), ("cu_seqlens_k", cu_k)):
+        if not isinstance(c, torch.Tensor) or c.dtype != torch.int32 or c.dim() != 1 or c.device != q_t.device:
+            raise ValueError(f"{name} must be an int32 [B + 1] tensor on the inputs' device")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    hq_t, d_t = q_t.shape[1], q_t.shape[2]
+    hk_t, hq_s, d_s, hk_s = k_t.shape[1], q_s.shape[1], q_s.shape[2], k_s.shape[1]
+    if k_t.shape[2] != d_t or k_s.shape[2] != d_s or q_s.shape[0] != q_t.shape[0] or k_s.shape[0] != k_t.shape[0]:
+        raise ValueError("inconsistent packed shapes: q_t [Tq,Hqt,dt], k_t [Tk,Hkt,dt], q_s [Tq,Hqs,ds], "
+                         "k_s [Tk,Hks,ds]")
+    H = max(hq_t, hq_s)
+    if H % hq_t or H % hq_s or hq_t % hk_t or hq_s % hk_s:
+        raise ValueError("head counts must nest as for grouped heads")
+    strides = (ctypes.c_int64 * 12)(*[s for t in ts for s in (0, t.stride(1), t.stride(0))])
+    return (cu_q.numel() - 1, H, int(max_q), int(max_k), d_t, d_s), strides, (hq_t, hk_t, hq_s, hk_s)
+
+
+def streamkl_fwd_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                        tau_t=None, tau_s=None, causal=False, with_sum=True):
+    """Forward over packed sequences: q_* [total_q, heads, d], k_* [total_k,
+    heads, d], batch b owning rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1.
+    Returns (kl_rows, lse_t, lse_s, kl_sum) with the per-row outputs padded
+    to [B, H, max_seqlen_q] (rows past a sequence's length are 0)."""
+    import torch
+    lib = load_library()
+    (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k,
+                                                                 max_seqlen_q, max_seqlen_k)
+    tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
+    dev = q_t.device
+    kl = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
+    lt, ls = torch.empty_like(kl), torch.empty_like(kl)
+    tot = torch.empty((1,), dtype=torch.float32, device=dev) if with_sum else None
+    lay = StreamKLLayout(*heads, None, None, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr())
+    code = lib.streamkl_fwd_ex(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t), B, H,
+                               n_q, n_k, d_t, d_s, strides, ctypes.byref(lay), tau_t, tau_s, int(bool(causal)),
+                               kl.data_ptr(), lt.data_ptr(), ls.data_ptr(), tot.data_ptr() if tot is not None else None,
+                               _stream_ptr(dev))
+    _check("streamkl_fwd_ex", code)
+    return kl, lt, ls, tot
+
+
+def streamkl_bwd_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, lse_t, lse_s,
+                        grad_rows=None, grad_scalar=1.0, tau_t=None, tau_s=None, causal=False, teacher=False,
+                        kl_rows=None):
+    """Backward over packed sequences: (dq, dk) packed like the inputs of the
+    differentiated model (the student, or the teacher if teacher=True, which
+    needs the forward's kl_rows).  Per-row arrays are [B, H, max_seqlen_q].
+    Only rows some sequence owns are written."""
+    import torch
+    lib = load_library()
+    (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k,
+                                                                 max_seqlen_q, max_seqlen_k)
+    tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
+    dev = q_t.device
+    rowargs = (("lse_t", lse_t), ("lse_s", lse_s)) + ((("kl_rows", kl_rows),) if teacher else ()) + \
+        ((("grad_rows", grad_rows),) if grad_rows is not None else ())
+    for name, t in rowargs:
+        if t is None or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, n_q):
+            raise ValueError(f"{name} must be a contiguous fp32 [B, H, max_seqlen_q] tensor")
+    if teacher:
+        dq = torch.empty((q_t.shape[0], heads[0], d_t), dtype=q_t.dtype, device=dev)
+        dk = torch.empty((k_t.shape[0], heads[1], d_t), dtype=q_t.dtype, device=dev)
+    else:
+        dq = torch.empty((q_s.shape[0], heads[2], d_s), dtype=q_s.dtype, device=dev)
+        dk = torch.empty((k_s.shape[0], heads[3], d_s), dtype=q_s.dtype, device=dev)
+    lay = StreamKLLayout(*heads, None, None, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr())
+    args = [q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t), B, H, n_q, n_k, d_t,
+            d_s, strides, ctypes.byref(lay), tau_t, tau_s, int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr()]
+    g = grad_rows.data_ptr() if grad_rows is not None else None
+    if teacher:
+        code = lib.streamkl_bwd_teacher_ex(*args, kl_rows.data_ptr(), g, float(grad_scalar), dq.data_ptr(),
+                                           dk.data_ptr(), None, 0, _stream_ptr(dev))
+        _check("streamkl_bwd_teacher_ex", code)
+    else:
+        code = lib.streamkl_bwd_ex(*args, g, float(grad_scalar), dq.data_ptr(), dk.data_ptr(), None, 0,
+                                   _stream_ptr(dev))
+        _check("streamkl_bwd_ex", code)
+    return dq, dk
+
+
 def _autograd_function():
     import torch
 
@@ -555,6 +649,9 @@ def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, seqle
     return _fn_cache.apply(q_t, k_t, q_s, k_s, tau_t, tau_s, causal, seqlen_q, seqlen_k)
 
 
-__all__ = ["streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
-           "attention_kl", "streamkl_vocab_fwd", "streamkl_vocab_bwd", "streamkl_vocab_fwd_bwd", "vocab_kl", "load_library", "supported", "status_string",
-           "StreamKLError", "STREAMKL_F32", "STREAMKL_BF16"]
+__all__ = [
+    "streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
+    "attention_kl", "streamkl_fwd_varlen", "streamkl_bwd_varlen", "streamkl_vocab_fwd", "streamkl_vocab_bwd",
+    "streamkl_vocab_fwd_bwd", "vocab_kl", "load_library", "supported", "status_string", "StreamKLError",
+    "STREAMKL_F32", "STREAMKL_BF16"
+]

@@ -235,6 +235,8 @@ struct FwdParams {
     // k_s); per-batch valid lengths (null: n_q, n_k)
     int g_qt, g_kt, g_qs, g_ks;
     const int *len_q, *len_k;
+    // packed sequences: batch b's rows start at row cu[b] (null: padded)
+    const int *cu_q, *cu_k;
 };
 
 // Valid length of batch b from a per-batch array (null: the full length),
@@ -243,6 +245,19 @@ __device__ inline int batch_len(const int *len, int b, int n) {
     if (!len) return n;
     const int v = len[b];
     return v < 0 ? 0 : (v > n ? n : v);
+}
+
+// First row and valid length of batch b: packed sequences (cu = offsets
+// [B + 1]) or padded ones (row 0, the length from `len` or n), clamped to n.
+__device__ inline void batch_rows(const int *cu, const int *len, int b, int n, int &row0, int &nb) {
+    if (cu) {
+        row0 = cu[b];
+        const int v = cu[b + 1] - row0;
+        nb = v < 0 ? 0 : (v > n ? n : v);
+    } else {
+        row0 = 0;
+        nb = batch_len(len, b, n);
+    }
 }
 
 // Scheduler group masks of __builtin_amdgcn_sched_group_barrier.
@@ -370,8 +385,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     const T *Qs = static_cast<const T *>(p.q_s) + bb * p.st[6] + (hh / p.g_qs) * p.st[7];
     const T *Ks = static_cast<const T *>(p.k_s) + bb * p.st[9] + (hh / p.g_ks) * p.st[10];
     const int64_t sqt = p.st[2], skt = p.st[5], sqs = p.st[8], sks = p.st[11];
-    // valid rows of this batch; the per-row outputs keep the full n_q stride
-    const int n_q = batch_len(p.len_q, bb, p.n_q), n_k = batch_len(p.len_k, bb, p.n_k), off = n_k - n_q;
+    // valid rows of this batch (and, for packed sequences, where they start);
+    // the per-row outputs keep the full n_q stride
+    int rq0, rk0, n_q, n_k;
+    batch_rows(p.cu_q, p.len_q, bb, p.n_q, rq0, n_q);
+    batch_rows(p.cu_k, p.len_k, bb, p.n_k, rk0, n_k);
+    const int off = n_k - n_q;
+    Qt += (int64_t)rq0 * sqt;
+    Qs += (int64_t)rq0 * sqs;
+    Kt += (int64_t)rk0 * skt;
+    Ks += (int64_t)rk0 * sks;
 
     const int q0w = qb * kBlockX + w * kTile;  // first query of this wave
     const int q = q0w + l32;                   // this lane's query
@@ -566,6 +589,7 @@ struct BwdParams {
     // output has Hout heads, output head o sums KL heads [o group, (o + 1) group)
     int g_xt, g_xs, g_yt, g_ys, Hout, group;
     const int *len_q, *len_k;  // per-batch valid lengths (null: n_q, n_k)
+    const int *cu_q, *cu_k;    // packed sequences: batch offsets [B + 1] (null: padded)
     // a group split over nsplit blocks of hsplit KL heads each, which write
     // fp32 partial gradients [nsplit][B Hout][n_x][DG] to `partial` (a later
     // launch sums them); n_xblk then counts n_x blocks times nsplit
@@ -774,19 +798,24 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // output head `bh` (of B Hout): batch bb, head ho, fed by KL heads ho group + u
     const int ho = bh % p.Hout, bb = bh / p.Hout;
+    const int64_t sxt = p.st[2], sxs = p.st[5], syt = p.st[8], sys = p.st[11];
+    // valid lengths of this batch (the arrays keep the full n_q / n_x strides)
+    // and, for packed sequences, the rows where they start
+    int rq0, rk0, n_qb, n_kb;
+    batch_rows(p.cu_q, p.len_q, bb, p.n_q, rq0, n_qb);
+    batch_rows(p.cu_k, p.len_k, bb, p.n_k, rk0, n_kb);
+    const int rx0 = DKMODE ? rk0 : rq0, ry0 = DKMODE ? rq0 : rk0;
+    const bool packed_x = (DKMODE ? p.cu_k : p.cu_q) != nullptr;
+    const int n_x = DKMODE ? n_kb : n_qb, n_y = DKMODE ? n_qb : n_kb, n_q = n_qb, off = n_kb - n_qb;
     const T *Xt, *Xs, *Yt, *Ys;  // the current KL head's tensors
     int64_t rowbase;              // per-query arrays of the current KL head
     auto set_head = [&](int hh) {
-        Xt = static_cast<const T *>(p.x_t) + bb * p.st[0] + (hh / p.g_xt) * p.st[1];
-        Xs = static_cast<const T *>(p.x_s) + bb * p.st[3] + (hh / p.g_xs) * p.st[4];
-        Yt = static_cast<const T *>(p.y_t) + bb * p.st[6] + (hh / p.g_yt) * p.st[7];
-        Ys = static_cast<const T *>(p.y_s) + bb * p.st[9] + (hh / p.g_ys) * p.st[10];
+        Xt = static_cast<const T *>(p.x_t) + bb * p.st[0] + (hh / p.g_xt) * p.st[1] + (int64_t)rx0 * sxt;
+        Xs = static_cast<const T *>(p.x_s) + bb * p.st[3] + (hh / p.g_xs) * p.st[4] + (int64_t)rx0 * sxs;
+        Yt = static_cast<const T *>(p.y_t) + bb * p.st[6] + (hh / p.g_yt) * p.st[7] + (int64_t)ry0 * syt;
+        Ys = static_cast<const T *>(p.y_s) + bb * p.st[9] + (hh / p.g_ys) * p.st[10] + (int64_t)ry0 * sys;
         rowbase = ((int64_t)bb * p.H + hh) * p.n_q;
     };
-    const int64_t sxt = p.st[2], sxs = p.st[5], syt = p.st[8], sys = p.st[11];
-    // valid lengths of this batch (the arrays keep the full n_q / n_x strides)
-    const int n_qb = batch_len(p.len_q, bb, p.n_q), n_kb = batch_len(p.len_k, bb, p.n_k);
-    const int n_x = DKMODE ? n_kb : n_qb, n_y = DKMODE ? n_qb : n_kb, n_q = n_qb, off = n_kb - n_qb;
 
     const int x0w = xb * kBlockX + w * kTile;
     const int x = x0w + l32;
@@ -1009,8 +1038,11 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
                 *reinterpret_cast<f32x4 *>(prow + d0) = o;
             }
         }
-    } else if (x < p.n_x) {
-        T *orow = static_cast<T *>(p.out) + (((int64_t)bb * p.Hout + ho) * p.n_x + x) * DG;
+    } else if (packed_x ? xv : x < p.n_x) {
+        // padded outputs [B, Hout, n_x, DG] (rows past the valid length zeroed);
+        // packed outputs [rows, Hout, DG], only this batch's valid rows
+        T *orow = static_cast<T *>(p.out) + (packed_x ? ((int64_t)(rx0 + x) * p.Hout + ho) * DG
+                                                      : (((int64_t)bb * p.Hout + ho) * p.n_x + x) * DG);
 #pragma unroll
         for (int t = 0; t < DG / kTile; ++t) {
 #pragma unroll
@@ -1101,9 +1133,12 @@ struct Shape {
 struct Heads {
     int h[4];
     const int *len_q, *len_k;
+    const int *cu_q, *cu_k;  // packed query / key sequences
+    bool packed(int t) const { return (t % 2 == 0 ? cu_q : cu_k) != nullptr; }  // t: q_t, k_t, q_s, k_s
 };
 streamkl_status resolve_layout(const streamkl_layout *lay, int H, Heads &hd) {
     hd.len_q = hd.len_k = nullptr;
+    hd.cu_q = hd.cu_k = nullptr;
     for (int t = 0; t < 4; ++t) hd.h[t] = H;
     if (!lay) return STREAMKL_OK;
     const int given[4] = {lay->heads_q_t, lay->heads_k_t, lay->heads_q_s, lay->heads_k_s};
@@ -1118,8 +1153,14 @@ streamkl_status resolve_layout(const streamkl_layout *lay, int H, Heads &hd) {
         if (H % hq != 0 || hq % hk != 0) return STREAMKL_ERR_INVALID;
     }
     if (((uintptr_t)lay->seqlen_q) % 4 != 0 || ((uintptr_t)lay->seqlen_k) % 4 != 0) return STREAMKL_ERR_INVALID;
+    if (((uintptr_t)lay->cu_seqlens_q) % 4 != 0 || ((uintptr_t)lay->cu_seqlens_k) % 4 != 0)
+        return STREAMKL_ERR_INVALID;
+    // a kind is either packed (offsets) or padded with lengths, not both
+    if ((lay->cu_seqlens_q && lay->seqlen_q) || (lay->cu_seqlens_k && lay->seqlen_k)) return STREAMKL_ERR_INVALID;
     hd.len_q = lay->seqlen_q;
     hd.len_k = lay->seqlen_k;
+    hd.cu_q = lay->cu_seqlens_q;
+    hd.cu_k = lay->cu_seqlens_k;
     return STREAMKL_OK;
 }
 
@@ -1150,11 +1191,17 @@ streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, 
             st[3 * t + 1] = strides[3 * t + 1];
             st[3 * t + 2] = strides[3 * t + 2];
             if (st[3 * t + 0] < 0 || st[3 * t + 1] < 0 || st[3 * t + 2] < dims[t]) return STREAMKL_ERR_INVALID;
+        } else if (hd.packed(t)) {
+            // packed sequences, contiguous [rows, heads, d]
+            st[3 * t + 2] = (int64_t)hd.h[t] * dims[t];
+            st[3 * t + 1] = dims[t];
+            st[3 * t + 0] = 0;
         } else {
             st[3 * t + 2] = dims[t];
             st[3 * t + 1] = (int64_t)ns[t] * dims[t];
             st[3 * t + 0] = (int64_t)hd.h[t] * ns[t] * dims[t];
         }
+        if (hd.packed(t)) st[3 * t + 0] = 0;  // rows are located by the offsets alone
         if (((uintptr_t)ptrs[t]) % 16 != 0) return STREAMKL_ERR_INVALID;
         for (int k = 0; k < 3; ++k)
             if ((st[3 * t + k] * elt) % 16 != 0) return STREAMKL_ERR_INVALID;
@@ -1212,7 +1259,8 @@ bwd_launch_t pick_bwd2(int causal, bool gs, bool first, bool grp) {
     if (grp) {
         if (first) return causal ? launch_bwd<T, DT, DS, true, false, true, true>
                                  : launch_bwd<T, DT, DS, false, false, true, true>;
-        return causal ? launch_bwd<T, DT, DS, true, false, false, true> : launch_bwd<T, DT, DS, false, false, false, true>;
+        return causal ? launch_bwd<T, DT, DS, true, false, false, true>
+                      : launch_bwd<T, DT, DS, false, false, false, true>;
     }
     if (first) return causal ? launch_bwd<T, DT, DS, true, false, true> : launch_bwd<T, DT, DS, false, false, true>;
     if (gs) return causal ? launch_bwd<T, DT, DS, true, true, false> : launch_bwd<T, DT, DS, false, true, false>;
@@ -1252,6 +1300,7 @@ streamkl_status fwd_common(const void *q_t, const void *k_t, const void *q_s, co
     if (rc != STREAMKL_OK) return rc;
     p.g_qt = H / hd.h[0]; p.g_kt = H / hd.h[1]; p.g_qs = H / hd.h[2]; p.g_ks = H / hd.h[3];
     p.len_q = hd.len_q; p.len_k = hd.len_k;
+    p.cu_q = hd.cu_q; p.cu_k = hd.cu_k;
     p.q_t = q_t; p.k_t = k_t; p.q_s = q_s; p.k_s = k_s;
     p.H = H; p.nheads = B * H; p.n_q = n_q; p.n_k = n_k;
     p.n_qblk = (n_q + kBlockX - 1) / kBlockX;
@@ -1351,6 +1400,7 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
         p.Hout = first ? ht[xi] : hs2[xi];
         p.group = H / p.Hout;
         p.len_q = hd.len_q; p.len_k = hd.len_k;
+        p.cu_q = hd.cu_q; p.cu_k = hd.cu_k;
         p.H = H; p.nheads = B * p.Hout; p.n_q = n_q; p.n_k = n_k;
         p.n_x = dk ? n_k : n_q;
         p.n_y = dk ? n_q : n_k;
@@ -1394,7 +1444,8 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
         // blocks when the caller gave room for their partial sums
         const int dg = first ? d_t : d_s;
         int ns = 1, hs_ = cur.group;
-        group_split(cur.nheads * cur.n_xblk, cur.group, ns, hs_);
+        // (packed outputs are written by the blocks themselves, never split)
+        if (!hd.packed(pass)) group_split(cur.nheads * cur.n_xblk, cur.group, ns, hs_);
         if (ns > 1 && split_bytes(ns, cur.nheads, cur.n_x, dg) <= workspace_bytes && workspace) {
             cur.nsplit = ns;
             cur.hsplit = hs_;
@@ -1435,7 +1486,7 @@ size_t bwd_ex_workspace(int B, int H, int n_q, int n_k, int d_t, int d_s, const 
         const int group = H / hout, n_x = dk ? n_k : n_q;
         const int nblk = B * hout * ((n_x + kBlockX - 1) / kBlockX);
         int ns = 1, hsp = group;
-        group_split(nblk, group, ns, hsp);
+        if (!hd.packed(pass)) group_split(nblk, group, ns, hsp);
         if (ns > 1) need = std::max(need, split_bytes(ns, B * hout, n_x, first ? d_t : d_s));
     }
     return need;

@@ -202,8 +202,9 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
                                      void *dq_t, void *dk_t, void *stream);
 
 /*
- * Grouped heads and per-batch lengths.  The pages define the divergence per
- * query row of one teacher and one student attention map and say nothing of
+ * Grouped heads, per-batch lengths and packed sequences.  The pages define
+ * the divergence per query row of one teacher and one student attention map
+ * and say nothing of
  * how heads pair up when the two models, or the queries and keys of one
  * model, have different head counts; these entry points take the plainest
  * reading, the grouped-key convention.  There are H KL heads (the per-row
@@ -229,10 +230,23 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
  * (j <= i + seqlen_k[b] - seqlen_q[b]).  An empty row (past the valid length,
  * or left with no allowed key) has KL 0 and LSEs 0, and contributes no
  * gradient; gradient rows past the valid lengths are written as 0.
+ *
+ * Packed sequences: cu_seqlens_q (device int32 [B + 1], NULL = padded) makes
+ * the queries packed: batch b owns query rows cu_seqlens_q[b] ..
+ * cu_seqlens_q[b + 1] - 1 of q_t [rows, heads_q_t, d_t] and q_s [rows,
+ * heads_q_s, d_s] (n_q is then the longest sequence; longer ones are cut to
+ * it), and dq_s / dq_t come back packed the same way, contiguous, only the
+ * valid rows written.  cu_seqlens_k does the same for the keys.  The batch
+ * stride of a packed tensor is ignored (its rows are located by the
+ * offsets); NULL strides mean contiguous [rows, heads, d].  A kind is either
+ * packed or padded with lengths: seqlen_q together with cu_seqlens_q is
+ * INVALID.  The per-row outputs (KL, LSEs, upstream gradients) stay padded
+ * [B, H, n_q].
  */
 typedef struct {
     int heads_q_t, heads_k_t, heads_q_s, heads_k_s;  /* 0 means H */
     const int32_t *seqlen_q, *seqlen_k;               /* device [B], 4-byte aligned, or NULL */
+    const int32_t *cu_seqlens_q, *cu_seqlens_k;       /* device [B + 1], 4-byte aligned, or NULL */
 } streamkl_layout;
 
 /* streamkl_fwd with a layout (NULL layout = streamkl_fwd).  INVALID also for a

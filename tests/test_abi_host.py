@@ -260,3 +260,17 @@ def test_layout_entry_points_reject_bad_layouts_before_any_hip_call():
     assert n4 == 16 * 2 * 1 * 4096 * 128 * 4
     # the teacher's heads decide the teacher gradients' split: none here
     assert lib.streamkl_bwd_ex_workspace_size(2, 16, 4096, 4096, 128, 128, ctypes.byref(one), 1) == 0
+
+
+def test_packed_sequence_layout_is_validated_before_any_hip_call():
+    lib = skl.load_library()
+
+    def fwd(sq=None, sk=None, cq=None, ck=None):
+        lay = skl.StreamKLLayout(0, 0, 0, 0, sq, sk, cq, ck)
+        return lib.streamkl_fwd_ex(A, A + 0x100000, A + 0x200000, A + 0x300000, skl.STREAMKL_BF16, 2, 4, 100, 300,
+                                   128, 64, None, ctypes.byref(lay), 0.088, 0.125, 0, A + 0x400000, A + 0x500000,
+                                   A + 0x600000, None, None)
+    assert fwd(cq=A + 2) == INV                 # misaligned offsets
+    assert fwd(ck=A + 6) == INV
+    assert fwd(sq=A, cq=A + 64) == INV          # a kind cannot be both padded with lengths and packed
+    assert fwd(sk=A, ck=A + 64) == INV

@@ -282,3 +282,53 @@ def test_grouped_full_size_sampled(name, kv, resize):
         check_grad(dk[b, 0][keys], rdk, "bf16", "grouped full dk_s keys (summed over the group)")
     assert abs(float(tot.item()) - float(np.sum(kl))) <= 1e-6 * float(np.sum(np.abs(kl)))
     _identities_grouped(xo, dq, dk, w.H, kv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_sequences_match_padded_lengths(causal):
+    """Packed sequences (cu_seqlens offsets) give the same bits as the same
+    data laid out padded with per-batch lengths: per-row outputs, and the
+    student and teacher gradients on every valid row; grouped student keys."""
+    lq, lk = [100, 37, 200], [150, 37, 260]
+    if causal:
+        lk = [max(a, b) for a, b in zip(lq, lk)]
+    B, n_q, n_k = 3, max(lq), max(lk)
+    heads = (4, 4, 4, 2)
+    x = _draw(41 + causal, B, heads, n_q, n_k, 128, 64, "bf16")
+    for b in range(B):  # padding rows hold garbage the kernels must not read
+        for k, n in (("q_t", lq[b]), ("q_s", lq[b]), ("k_t", lk[b]), ("k_s", lk[b])):
+            x[k][b, :, n:] = 1e3
+    d = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    sq = torch.tensor(lq, dtype=torch.int32, device="cuda")
+    sk = torch.tensor(lk, dtype=torch.int32, device="cuda")
+    cq = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32, device="cuda")
+    ck = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32, device="cuda")
+
+    def pack(t, lens):
+        return torch.cat([t[b, :, :lens[b]].transpose(0, 1) for b in range(B)]).contiguous()
+    pk = {k: pack(d[k], lq if k.startswith("q") else lk) for k in d}
+    args = (d["q_t"], d["k_t"], d["q_s"], d["k_s"])
+    pargs = (pk["q_t"], pk["k_t"], pk["q_s"], pk["k_s"], cq, ck, n_q, n_k)
+    kl, lt, ls, tot = skl.streamkl_fwd(*args, causal=causal, seqlen_q=sq, seqlen_k=sk)
+    pkl, plt, pls, ptot = skl.streamkl_fwd_varlen(*pargs, causal=causal)
+    g = torch.from_numpy(np.random.default_rng(9).standard_normal((B, 4, n_q)).astype(np.float32)).cuda()
+    dq, dk = skl.streamkl_bwd(*args, lt, ls, grad_rows=g, causal=causal, seqlen_q=sq, seqlen_k=sk)
+    pdq, pdk = skl.streamkl_bwd_varlen(*pargs, plt, pls, grad_rows=g, causal=causal)
+    tdq, tdk = skl.streamkl_bwd_teacher(*args, lt, ls, kl, grad_rows=g, causal=causal, seqlen_q=sq, seqlen_k=sk)
+    ptdq, ptdk = skl.streamkl_bwd_varlen(*pargs, plt, pls, grad_rows=g, causal=causal, teacher=True, kl_rows=pkl)
+    torch.cuda.synchronize()
+    for a, b_ in ((kl, pkl), (lt, plt), (ls, pls), (tot, ptot)):
+        assert torch.equal(a, b_)
+    for padded, packed, lens in ((dq, pdq, lq), (tdq, ptdq, lq), (tdk, ptdk, lk)):
+        assert torch.equal(pack(padded, lens), packed)
+    # the grouped dK_s: the padded launch splits its head groups over blocks
+    # (fp32 partial sums added afterwards), the packed one never does, so the
+    # two agree to rounding rather than bit for bit
+    a, b_ = pack(dk, lk).float(), pdk.float()
+    assert (a - b_).norm() <= 2e-3 * a.norm()
+    # and the padded results match the oracle
+    t_t, t_s = float(np.float32(1 / np.sqrt(128))), float(np.float32(1 / np.sqrt(64)))
+    ref = _reference(x, 4, t_t, t_s, causal, lq, lk, g=g.cpu().numpy())
+    check_kl(kl.cpu().numpy(), ref["kl"], "bf16", "packed kl")
+    check_grad(dk.float().cpu().numpy(), ref["dk_s"], "bf16", "packed dk_s")
+    check_grad(tdq.float().cpu().numpy(), ref["dq_t"], "bf16", "packed dq_t")
