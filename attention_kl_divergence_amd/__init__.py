@@ -623,8 +623,56 @@ def _vocab_autograd_function():
     return VocabKLFunction
 
 
+def _varlen_autograd_function():
+    import torch
+
+    class StreamKLVarlenFunction(torch.autograd.Function):
+        """Per-row attention KL over packed sequences, with gradients for the
+        student tensors and, when they require them, the teacher tensors.
+        forward(q_t, k_t, q_s, k_s, cu_q, cu_k, max_q, max_k, tau_t, tau_s,
+        causal) -> kl_rows [B, H, max_q]"""
+
+        @staticmethod
+        def forward(ctx, q_t, k_t, q_s, k_s, cu_q, cu_k, max_q, max_k, tau_t=None, tau_s=None, causal=False):
+            kl, lt, ls, _ = streamkl_fwd_varlen(q_t, k_t, q_s, k_s, cu_q, cu_k, max_q, max_k, tau_t, tau_s, causal,
+                                                with_sum=False)
+            ctx.save_for_backward(q_t, k_t, q_s, k_s, cu_q, cu_k, lt, ls, kl)
+            ctx.cfg = (max_q, max_k, tau_t, tau_s, causal)
+            return kl
+
+        @staticmethod
+        def backward(ctx, g):
+            q_t, k_t, q_s, k_s, cu_q, cu_k, lt, ls, kl = ctx.saved_tensors
+            max_q, max_k, tau_t, tau_s, causal = ctx.cfg
+            g = g.to(torch.float32).contiguous()
+            dq_s = dk_s = dq_t = dk_t = None
+            common = (q_t, k_t, q_s, k_s, cu_q, cu_k, max_q, max_k, lt, ls)
+            if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+                dq_s, dk_s = streamkl_bwd_varlen(*common, grad_rows=g, tau_t=tau_t, tau_s=tau_s, causal=causal)
+            if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+                dq_t, dk_t = streamkl_bwd_varlen(*common, grad_rows=g, tau_t=tau_t, tau_s=tau_s, causal=causal,
+                                                 teacher=True, kl_rows=kl)
+            return dq_t, dk_t, dq_s, dk_s, None, None, None, None, None, None, None
+
+    return StreamKLVarlenFunction
+
+
 _fn_cache = None
+_varlen_fn_cache = None
 _vocab_fn_cache = None
+
+
+def attention_kl_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, tau_t=None,
+                        tau_s=None, causal=False):
+    """Differentiable per-row attention KL over packed sequences ([rows, heads,
+    d] tensors, int32 offsets [B + 1]); returns [B, H, max_seqlen_q], rows past
+    a sequence's length 0.  Rows of the packed gradients that no sequence owns
+    are left unwritten."""
+    global _varlen_fn_cache
+    if _varlen_fn_cache is None:
+        _varlen_fn_cache = _varlen_autograd_function()
+    return _varlen_fn_cache.apply(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q),
+                                  int(max_seqlen_k), tau_t, tau_s, causal)
 
 
 def vocab_kl(z_t, z_s, temperature=1.0):
@@ -651,7 +699,7 @@ def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, seqle
 
 __all__ = [
     "streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
-    "attention_kl", "streamkl_fwd_varlen", "streamkl_bwd_varlen", "streamkl_vocab_fwd", "streamkl_vocab_bwd",
-    "streamkl_vocab_fwd_bwd", "vocab_kl", "load_library", "supported", "status_string", "StreamKLError",
-    "STREAMKL_F32", "STREAMKL_BF16"
+    "attention_kl", "streamkl_fwd_varlen", "streamkl_bwd_varlen", "attention_kl_varlen", "streamkl_vocab_fwd",
+    "streamkl_vocab_bwd", "streamkl_vocab_fwd_bwd", "vocab_kl", "load_library", "supported", "status_string",
+    "StreamKLError", "STREAMKL_F32", "STREAMKL_BF16"
 ]

@@ -332,3 +332,29 @@ def test_packed_sequences_match_padded_lengths(causal):
     check_kl(kl.cpu().numpy(), ref["kl"], "bf16", "packed kl")
     check_grad(dk.float().cpu().numpy(), ref["dk_s"], "bf16", "packed dk_s")
     check_grad(tdq.float().cpu().numpy(), ref["dq_t"], "bf16", "packed dq_t")
+
+
+def test_packed_sequences_autograd():
+    """attention_kl_varlen under autograd gives the gradients of the explicit
+    packed calls, for student and teacher tensors."""
+    lq, lk = [50, 90], [70, 90]
+    cq = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32, device="cuda")
+    ck = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(50)
+    mk = lambda n, h, d: torch.from_numpy(rng.standard_normal((n, h, d), dtype=np.float32)).cuda()
+    q_t, k_t, q_s, k_s = mk(sum(lq), 4, 64), mk(sum(lk), 2, 64), mk(sum(lq), 4, 64), mk(sum(lk), 1, 64)
+    leaves = [t.clone().requires_grad_(True) for t in (q_t, k_t, q_s, k_s)]
+    kl = skl.attention_kl_varlen(*leaves, cq, ck, max(lq), max(lk), causal=True)
+    w = torch.linspace(0.5, 1.5, kl.numel(), device="cuda").reshape(kl.shape)
+    (kl * w).sum().backward()
+    torch.cuda.synchronize()
+    _, lt, ls, _ = skl.streamkl_fwd_varlen(q_t, k_t, q_s, k_s, cq, ck, max(lq), max(lk), causal=True)
+    ref_s = skl.streamkl_bwd_varlen(q_t, k_t, q_s, k_s, cq, ck, max(lq), max(lk), lt, ls, grad_rows=w.contiguous(),
+                                    causal=True)
+    kl2, _, _, _ = skl.streamkl_fwd_varlen(q_t, k_t, q_s, k_s, cq, ck, max(lq), max(lk), causal=True)
+    ref_t = skl.streamkl_bwd_varlen(q_t, k_t, q_s, k_s, cq, ck, max(lq), max(lk), lt, ls, grad_rows=w.contiguous(),
+                                    causal=True, teacher=True, kl_rows=kl2)
+    torch.cuda.synchronize()
+    for got, ref in ((leaves[2].grad, ref_s[0]), (leaves[3].grad, ref_s[1]), (leaves[0].grad, ref_t[0]),
+                     (leaves[1].grad, ref_t[1])):
+        assert torch.equal(got, ref)
