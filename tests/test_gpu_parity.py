@@ -281,3 +281,39 @@ def test_sharp_and_rising_scores_force_reference_moves(dtype):
     if dtype == "bf16":
         x2 = {k: inputs.round_bf16(v) for k, v in x2.items()}
     _full_compare(w, x2)
+
+
+def test_concurrent_host_threads_and_streams():
+    """The library keeps no mutable global state: four host threads, each on
+    its own stream, give the same bits as one thread."""
+    import threading
+    w = W["corr_4k"].resized(B=1, H=4, n_q=300, n_k=400, seed=240)
+    d = to_device(inputs.make(w), w.dtype)
+    args = (d["q_t"], d["k_t"], d["q_s"], d["k_s"])
+    kl0, lt0, ls0, _ = skl.streamkl_fwd(*args, causal=True)
+    dq0, dk0 = skl.streamkl_bwd(*args, lt0, ls0, causal=True)
+    torch.cuda.synchronize()
+    results, errors = [None] * 4, []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = []
+                for _ in range(3):
+                    kl, lt, ls, _ = skl.streamkl_fwd(*args, causal=True)
+                    dq, dk = skl.streamkl_bwd(*args, lt, ls, causal=True)
+                    outs.append((kl, dq, dk))
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:  # reported below
+            errors.append(e)
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+    for outs in results:
+        for kl, dq, dk in outs:
+            assert torch.equal(kl, kl0) and torch.equal(dq, dq0) and torch.equal(dk, dk0)
