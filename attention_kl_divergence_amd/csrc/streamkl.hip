@@ -54,7 +54,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 // Stand-in score for a masked key: finite, so that 0 * score stays 0 and the
 // running max of a lane that has seen no allowed key yet stays finite.
 constexpr float kMasked = -1.0e30f;
@@ -168,25 +167,58 @@ struct Tile {
 };
 
 // Rows [row0, row0 + kBN) of a [n, D] row-major matrix (row stride in elements)
-// into an LDS tile, by direct global->LDS loads.  Rows past the end repeat the
+// into an LDS tile, by direct buffer->LDS loads.  Rows past the end repeat the
 // last row: they are always masked out before use, and finite values keep
 // 0 * value = 0 in the contractions.
+//
+// The lane's part of every tile is fixed: DmaLanes holds, per load, the byte
+// offset of the lane's chunk from the tile's first row, computed once per
+// kernel.  Each tile then costs one wave-uniform buffer descriptor (scalar
+// arithmetic) whose base is the tile's first row and whose size ends at its
+// last valid row, so the hardware bounds every load to the tile.  The host
+// keeps 32 row strides below 2^31 bytes, so the offsets fit in 32 bits.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+
 template <typename T, int D>
-__device__ inline void dma_tile(const T *base, int64_t stride_n, int row0, int nrows, char *tile, int wv, int lane) {
+struct DmaLanes {
     using L = Tile<T, D>;
-    constexpr int kSlots = L::kBytes / 1024;  // 1 KiB per wave instruction
-    constexpr int kPerWave = (kSlots + kWaves - 1) / kWaves;
+    static constexpr int kSlots = L::kBytes / 1024;  // 1 KiB per wave instruction
+    static constexpr int kPerWave = (kSlots + kWaves - 1) / kWaves;
+    uint32_t off[kPerWave];
+    uint32_t sb;  // row stride in bytes
+    __device__ inline DmaLanes(int64_t stride_n, int wv, int lane) {
+        sb = (uint32_t)(stride_n * Ty<T>::kBytes);
 #pragma unroll
-    for (int k = 0; k < kPerWave; ++k) {
+        for (int k = 0; k < kPerWave; ++k) {
+            const int pos = (k * kWaves + wv) * 64 + lane;  // chunk slot this lane fills
+            const int r = pos / L::kChunks;
+            const int c = (pos % L::kChunks) ^ L::swz(r);
+            off[k] = (uint32_t)r * sb + (uint32_t)c * 16u;
+        }
+    }
+};
+
+template <typename T, int D>
+__device__ inline void dma_tile(const DmaLanes<T, D> &ln, const T *base, int64_t stride_n, int row0, int nrows,
+                                char *tile, int wv, int lane) {
+    using L = Tile<T, D>;
+    using DL = DmaLanes<T, D>;
+    const int last = min(nrows - 1 - row0, kBN - 1);  // last row of the tile that exists (wave-uniform)
+    if (last < 0) return;                              // no row (callers never ask for such a tile)
+    const char *g0 = reinterpret_cast<const char *>(base + (int64_t)row0 * stride_n);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(g0), (short)0,
+                                                        (int)((uint32_t)last * ln.sb + L::kRowBytes), kBufferWord3);
+#pragma unroll
+    for (int k = 0; k < DL::kPerWave; ++k) {
         const int slot = k * kWaves + wv;  // wave-uniform
-        if (kSlots % kWaves != 0 && slot >= kSlots) break;
-        const int pos = slot * 64 + lane;  // chunk slot this lane fills
-        const int r = pos / L::kChunks;
-        const int c = (pos % L::kChunks) ^ L::swz(r);
-        int gr = row0 + r;
-        gr = gr < nrows ? gr : nrows - 1;
-        const char *g = reinterpret_cast<const char *>(base + (int64_t)gr * stride_n) + c * 16;
-        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(tile + slot * 1024), 16, 0, 0);
+        if (DL::kSlots % kWaves != 0 && slot >= DL::kSlots) break;
+        uint32_t o = ln.off[k];
+        if (last < kBN - 1) {  // a tile crossing the end: rows past it read the last row
+            const int r = (slot * 64 + lane) / L::kChunks;
+            if (r > last) o -= (uint32_t)(r - last) * ln.sb;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(tile + slot * 1024),
+                                                 16, o, 0, 0, 0);
     }
 }
 
@@ -414,9 +446,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
         const int k0 = (t0 + t) * kBN;
         return (k0 + kBN > n_k) || (CAUSAL && k0 + kBN - 1 > q0w + off);
     };
+    const DmaLanes<T, DT> lanes_t(skt, w, lane);
+    const DmaLanes<T, DS> lanes_s(sks, w, lane);
     auto issue = [&](int t, char *stage) {
-        dma_tile<T, DT>(Kt, skt, (t0 + t) * kBN, n_k, stage, w, lane);
-        dma_tile<T, DS>(Ks, sks, (t0 + t) * kBN, n_k, stage + TileT::kBytes, w, lane);
+        dma_tile<T, DT>(lanes_t, Kt, skt, (t0 + t) * kBN, n_k, stage, w, lane);
+        dma_tile<T, DS>(lanes_s, Ks, sks, (t0 + t) * kBN, n_k, stage + TileT::kBytes, w, lane);
     };
 
     if (ntile > 0) issue(0, smem);
@@ -839,14 +873,16 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         return m;
     };
     const int nstage = (ntile + kBwdSub - 1) / kBwdSub;
+    const DmaLanes<T, DT> lanes_t(syt, w, lane);
+    const DmaLanes<T, DS> lanes_s(sys, w, lane);
     auto issue = [&](int st, int stage) {
 #pragma unroll
         for (int sub = 0; sub < kBwdSub; ++sub) {
             const int t = st * kBwdSub + sub;
             if (t < ntile) {
                 char *base = smem + stage * STAGE + sub * PAIR;
-                dma_tile<T, DT>(Yt, syt, ystart + t * kBN, n_y, base, w, lane);
-                dma_tile<T, DS>(Ys, sys, ystart + t * kBN, n_y, base + TileT::kBytes, w, lane);
+                dma_tile<T, DT>(lanes_t, Yt, syt, ystart + t * kBN, n_y, base, w, lane);
+                dma_tile<T, DS>(lanes_s, Ys, sys, ystart + t * kBN, n_y, base + TileT::kBytes, w, lane);
             }
         }
     };
@@ -1203,6 +1239,8 @@ streamkl_status check_common(const void *q_t, const void *k_t, const void *q_s, 
         }
         if (hd.packed(t)) st[3 * t + 0] = 0;  // rows are located by the offsets alone
         if (((uintptr_t)ptrs[t]) % 16 != 0) return STREAMKL_ERR_INVALID;
+        // streamed tiles address 32 rows with 32-bit offsets
+        if (st[3 * t + 2] * elt >= ((int64_t)1 << 26)) return STREAMKL_ERR_INVALID;
         for (int k = 0; k < 3; ++k)
             if ((st[3 * t + k] * elt) % 16 != 0) return STREAMKL_ERR_INVALID;
     }

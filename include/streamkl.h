@@ -30,7 +30,9 @@
  *  - Inputs are [B, H, N, d] with the last dimension contiguous.  `strides`
  *    gives, in ELEMENTS, the batch, head and row strides of q_t, k_t, q_s, k_s in
  *    that order (12 values: q_t.b, q_t.h, q_t.n, k_t.b, ...); NULL means fully
- *    contiguous.  Every row must start on a 16-byte boundary.
+ *    contiguous.  Every row must start on a 16-byte boundary, and the row
+ *    stride times the element size must be below 2^26 bytes (64 MiB; the
+ *    kernels address a 32-row tile with 32-bit offsets).
  *  - Teacher and student share dtype, B, H, n_q and n_k; d_t and d_s may differ.
  *  - Per-row outputs (kl_rows, lse_t, lse_s, grad_rows) are contiguous fp32
  *    [B, H, n_q].  Gradients dq_s / dk_s are contiguous [B, H, n_q | n_k, d_s]

@@ -83,6 +83,8 @@ INV, UNS = skl.STREAMKL_ERR_INVALID, skl.STREAMKL_ERR_UNSUPPORTED
     (dict(strides=[3 * 100 * 128, 100 * 128, 120] + [0, 0, 128] * 3), INV),  # 120 bf16 = 240 B ok, k_t b/h 0 ok ...
     (dict(strides=[3 * 100 * 128, 100 * 128, 100] + [0, 0, 128] * 3), INV),  # row stride < d_t
     (dict(strides=[3 * 100 * 128, 100 * 128, 132] + [0, 0, 128] * 3), INV),  # 264 B rows, not 16-B aligned
+    (dict(strides=[0, 0, 128] * 3 + [0, 0, 1 << 25]), INV),  # k_s rows 64 MiB apart: tile offsets past 32 bits
+    (dict(strides=[0, 0, 1 << 25] + [0, 0, 128] * 3, dtype=skl.STREAMKL_F32, d_t=64), INV),  # 128 MiB fp32 rows
     (dict(B=1024, H=1024, n_q=4096, n_k=4096), INV),  # 2^20 heads x 64 blocks x 256 threads >= 2^32 work-items
     (dict(n_q=(1 << 30), n_k=(1 << 30), B=1, H=1), INV),  # row indices beyond 32-bit kernel arithmetic
 ])
