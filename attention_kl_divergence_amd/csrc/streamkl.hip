@@ -383,6 +383,11 @@ __device__ inline void online_step(Online &o, const f32x16 &xt, const f32x16 &xs
         at = fmaf(et, xt[i], at);
         as = fmaf(et, xs[i], as);
     }
+    // Only the common branch below uses at and as, so the compiler would sink
+    // their 32 FMAs past the branch, out of the block whose MFMAs they are
+    // scheduled to hide under.  An empty statement that reads them keeps them
+    // here (it emits no instruction).
+    asm volatile("" ::"v"(at), "v"(as));
     const bool fine = (lt < 0x1p64f) && (ls < 0x1p64f);
     if (__builtin_amdgcn_ballot_w64(!fine) != 0) {
         online_update<false, CAUSAL>(o, xt, xs, ct, cs, k0, hf, q, n_k, off);
