@@ -159,6 +159,37 @@ def test_strided_views_match_contiguous():
         assert torch.equal(a, b)
 
 
+def test_rows_just_under_the_stride_limit_match_contiguous():
+    """Rows 2^26 - 128 bytes apart, the largest row stride the library takes: a
+    32-row tile then spans nearly 2^31 bytes of 32-bit offsets.  Three key tiles
+    (the last one ragged) and two query tiles, forward and both gradient kinds,
+    bit for bit against contiguous copies."""
+    w = W["mixed_dims_2k"].resized(B=1, H=1, n_q=40, n_k=70, seed=215)
+    x = inputs.make(w)
+    d = to_device(x, "bf16")
+    S = (1 << 25) - 64  # elements: 2^26 - 128 bytes of bf16
+
+    def far(t):
+        B, H, N, D = t.shape
+        buf = torch.empty((N, S), dtype=t.dtype, device=t.device)
+        buf[:, :D] = t[0, 0]
+        return buf[:, :D].view(1, 1, N, D)
+
+    v = {k: far(t) for k, t in d.items()}
+    assert v["k_s"].stride(2) == S
+    ref = skl.streamkl_fwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], w.tau_t, w.tau_s, False)
+    ref_g = skl.streamkl_bwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"], ref[1], ref[2], tau_t=w.tau_t, tau_s=w.tau_s)
+    got = skl.streamkl_fwd(v["q_t"], v["k_t"], v["q_s"], v["k_s"], w.tau_t, w.tau_s, False)
+    got_g = skl.streamkl_bwd(v["q_t"], v["k_t"], v["q_s"], v["k_s"], got[1], got[2], tau_t=w.tau_t, tau_s=w.tau_s)
+    torch.cuda.synchronize()
+    for a, b in zip(ref[:3], got[:3]):
+        assert torch.equal(a, b)
+    for a, b in zip(ref_g, got_g):
+        assert torch.equal(a, b)
+    del v
+    torch.cuda.empty_cache()
+
+
 def test_deterministic_bitwise():
     w = W["corr_4k"].resized(B=2, H=4, n_q=513, n_k=700, seed=210)
     d = to_device(inputs.make(w), "bf16")
