@@ -101,6 +101,27 @@ def test_streamed_tiles_use_buffer_loads_into_lds(asm):
         assert not any(o.startswith("global_load_lds") for o in ops), name
 
 
+def test_forward_fast_path_keeps_its_fmas_beside_the_mfmas(asm):
+    """In every bf16 forward kernel, the steady-state block that issues the next
+    tile's MFMAs and this tile's 32 exponentials also holds all 64 FMAs of the
+    tile (32 scale-shifts, 32 teacher-weighted sums): none is sunk past the
+    rebase branch into a serial tail where no MFMA hides it."""
+    starts = [(i, l.split(":")[0]) for i, l in enumerate(asm)
+              if re.match(r"^_ZN12_GLOBAL__N_1\d+streamkl_fwd_kernelIDF16b\w*:", l)]
+    assert len(starts) == 8
+    for i, name in starts:
+        end = next(j for j in range(i, len(asm)) if asm[j].startswith(".Lfunc_end"))
+        best, ops = 0, []
+        for line in asm[i:end] + [".LBBend:"]:
+            if re.match(r"^\.LBB\d+_\d+:|^\.LBBend:|^; %bb", line):
+                if sum(o == "v_exp_f32_e32" for o in ops) >= 32 and any(o.startswith("v_mfma") for o in ops):
+                    best = max(best, sum(o in ("v_fma_f32", "v_fmac_f32_e32") for o in ops))
+                ops = []
+            elif line.startswith("\t"):
+                ops.append(line.strip().split(" ")[0])
+        assert best >= 64, f"{name}: {best} FMAs in the MFMA block"
+
+
 def test_vocab_kernels_do_not_spill_and_stay_vectorised(tmp_path):
     """The vocabulary-logit kernels stream HBM: no register spills (private
     segment 0) in any instantiation, and the vector paths move the logits with
