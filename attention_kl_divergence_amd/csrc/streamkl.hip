@@ -98,7 +98,7 @@ template <> struct Ty<float> {
     static constexpr int ksteps(int D) { return D / 2; }
 };
 
-// Barrier that publishes tiles filled by direct global->LDS loads.  Those loads
+// Barrier that publishes tiles filled by direct buffer->LDS loads.  Those loads
 // count on the wave's vmcnt, and a workgroup barrier alone does not wait for
 // them, so every wave first drains its own loads (vmcnt(0), lgkmcnt(0)); after
 // the barrier every wave's share of the tiles is in LDS.
@@ -151,8 +151,8 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // on the 64-bank LDS: 16 lanes reading the same chunk of 16 consecutive rows
 // (MFMA operand rows), and 16 lanes reading 32 contiguous bytes from each of 4
 // consecutive rows (the transpose reads of the backward).  Tiles are filled by
-// direct global->LDS loads, which place lane i's 16 bytes at slot base + 16 i,
-// so each lane fetches the global chunk that belongs at its slot.
+// direct buffer->LDS loads, which place lane i's 16 bytes at slot base + 16 i,
+// so each lane fetches the chunk of HBM that belongs at its slot.
 template <typename T, int D>
 struct Tile {
     static constexpr int kRowBytes = D * Ty<T>::kBytes;
@@ -400,7 +400,7 @@ __device__ inline void online_step(Online &o, const f32x16 &xt, const f32x16 &xs
 }
 
 // One block = kWaves waves x 32 queries.  The key tiles stream through a two-stage
-// LDS ring filled by direct global->LDS loads; in steady state the MFMAs of
+// LDS ring filled by direct buffer->LDS loads; in steady state the MFMAs of
 // tile j+1 are issued interleaved with the exponentials and sums of tile j
 // (which only need registers) while the loads of tile j+2 are in flight.
 template <typename T, int DT, int DS, bool CAUSAL>
