@@ -56,7 +56,8 @@ extern "C" {
 typedef enum {
     STREAMKL_OK = 0,
     STREAMKL_ERR_INVALID = 1,     /* null pointer, bad size, bad tau, misalignment, causal with n_q > n_k,
-                                     or a problem too large for one dispatch (B H (ceil(n_q/128) +
+                                     a row stride of 2^26 bytes or more, or a problem too large for one
+                                     dispatch (B H (ceil(n_q/128) +
                                      ceil(n_k/128)) 256 >= 2^32, or n_q / n_k beyond 2^30 - 128) */
     STREAMKL_ERR_UNSUPPORTED = 2, /* (dtype, d_t, d_s) combination not built */
     STREAMKL_ERR_WORKSPACE = 3,   /* workspace too small (streamkl_fwd_split) */
