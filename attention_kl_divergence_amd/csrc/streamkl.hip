@@ -803,7 +803,7 @@ __device__ inline void tile_grad(f32x16 *G, const float *dsv, const void *trf, c
 }
 
 #ifndef STREAMKL_TR_EARLY
-#define STREAMKL_TR_EARLY 1  // k-steps of transposed operands read before the dS arithmetic
+#define STREAMKL_TR_EARLY 0  // k-steps of transposed operands read before the dS arithmetic (0, 1 or 2; 0 measured best)
 #endif
 #ifndef STREAMKL_BWD_SUB
 #define STREAMKL_BWD_SUB 2
@@ -963,7 +963,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
         const int y0 = ystart + it * kBN;
         const float *rv = &rowv[DKMODE ? stage : 0][0][DKMODE ? sub * kBN : 0];
         const char *ys = smem + stage * STAGE + sub * PAIR + GOFF;
-        // the transposed operand reads go out before the dS arithmetic hides them
+        // EARLY k-steps of the transposed operand reads can go out before the dS
+        // arithmetic (which then hides their latency); the rest follow it
         TrFrags<(sizeof(T) == 2 ? DG : kTile)> trf;
         if constexpr (sizeof(T) == 2) {
             if (EARLY > 0) {
