@@ -805,6 +805,9 @@ __device__ inline void tile_grad(f32x16 *G, const float *dsv, const void *trf, c
 #ifndef STREAMKL_TR_EARLY
 #define STREAMKL_TR_EARLY 0  // k-steps of transposed operands read before the dS arithmetic (0, 1 or 2; 0 measured best)
 #endif
+// The grouped-head kernels keep more state live across their head loop: with
+// one k-step read early they spill less at the head boundaries.
+constexpr int kTrEarlyGrouped = 1;
 #ifndef STREAMKL_BWD_SUB
 #define STREAMKL_BWD_SUB 2
 #endif
@@ -1011,7 +1014,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
             if (PLAIN) {
                 const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
                 const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
-                ds_grad(cur_t, cur_s, it, sc, sub, false, std::integral_constant<int, STREAMKL_TR_EARLY>{});
+                ds_grad(cur_t, cur_s, it, sc, sub, false,
+                        std::integral_constant<int, GRP ? kTrEarlyGrouped : STREAMKL_TR_EARLY>{});
             } else if (it < ntile && active(it)) {
                 const f32x16 cur_t = tile_scores<T, DT>(bc, xtv, l32, hf);
                 const f32x16 cur_s = tile_scores<T, DS>(bc + TileT::kBytes, xsv, l32, hf);
