@@ -19,7 +19,7 @@
  *  - same lecture, section 1: H(p,q) = H(p) + D_KL(p||q) (used by the tests
  *    as an independent cross-check, not here).
  *
- * Readings taken where the pages are silent (each listed in the design doc):
+ * Readings taken where the pages are silent (each also listed with the design notes):
  *  - scores are s = tau * (q . k), tau applied in fp64 after the dot product;
  *  - causal alignment is bottom-right: key j is allowed for query i iff
  *    j <= i + (n_k - n_q); causal with n_q > n_k is rejected by the caller;
