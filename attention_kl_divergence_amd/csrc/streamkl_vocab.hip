@@ -63,9 +63,17 @@ __device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 // ---------------------------------------------------------------- 8-logit I/O
 template <typename T> struct VIo;
+// NT: a non-temporal access (the logits of a row are read once per pass and
+// the gradients written once: streaming them past the caches leaves the
+// caches to the rest of the traffic).  The fused launch's first pass keeps
+// ordinary loads, so that its second pass finds the row in the caches.
 template <> struct VIo<bf16_t> {
     struct Raw { u32x4 v; };
-    __device__ static inline Raw load(const bf16_t *p) { return Raw{*reinterpret_cast<const u32x4 *>(p)}; }
+    template <bool NT = false>
+    __device__ static inline Raw load(const bf16_t *p) {
+        if constexpr (NT) return Raw{__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p))};
+        else return Raw{*reinterpret_cast<const u32x4 *>(p)};
+    }
     __device__ static inline void widen(const Raw &r, float z[8]) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -76,6 +84,7 @@ template <> struct VIo<bf16_t> {
             z[2 * k + 1] = __builtin_bit_cast(float, u & 0xffff0000u);
         }
     }
+    template <bool NT = false>
     __device__ static inline void store(bf16_t *p, const float z[8]) {
         u32x4 o;
 #pragma unroll
@@ -84,7 +93,8 @@ template <> struct VIo<bf16_t> {
             o[k] = (unsigned)__builtin_bit_cast(unsigned short, lo) |
                    ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16);
         }
-        *reinterpret_cast<u32x4 *>(p) = o;
+        if constexpr (NT) __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(p));
+        else *reinterpret_cast<u32x4 *>(p) = o;
     }
     __device__ static inline float load1(const bf16_t *p) { return (float)*p; }
     __device__ static inline void store1(bf16_t *p, float z) { *p = (bf16_t)z; }
@@ -92,8 +102,11 @@ template <> struct VIo<bf16_t> {
 template <> struct VIo<float> {
     // fp32 logits are moved as float vectors: no bit casts of vector elements
     struct Raw { f32x4 a, b; };
+    template <bool NT = false>
     __device__ static inline Raw load(const float *p) {
-        return Raw{reinterpret_cast<const f32x4 *>(p)[0], reinterpret_cast<const f32x4 *>(p)[1]};
+        const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
+        if constexpr (NT) return Raw{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1)};
+        else return Raw{q[0], q[1]};
     }
     __device__ static inline void widen(const Raw &r, float z[8]) {
 #pragma unroll
@@ -102,10 +115,17 @@ template <> struct VIo<float> {
             z[4 + k] = r.b[k];
         }
     }
+    template <bool NT = false>
     __device__ static inline void store(float *p, const float z[8]) {
         const f32x4 a = {z[0], z[1], z[2], z[3]}, b = {z[4], z[5], z[6], z[7]};
-        reinterpret_cast<f32x4 *>(p)[0] = a;
-        reinterpret_cast<f32x4 *>(p)[1] = b;
+        f32x4 *q = reinterpret_cast<f32x4 *>(p);
+        if constexpr (NT) {
+            __builtin_nontemporal_store(a, q);
+            __builtin_nontemporal_store(b, q + 1);
+        } else {
+            q[0] = a;
+            q[1] = b;
+        }
     }
     __device__ static inline float load1(const float *p) { return *p; }
     __device__ static inline void store1(float *p, float z) { *p = z; }
@@ -220,7 +240,7 @@ template <typename T> __device__ inline int head_elems(const T *p) {
 }
 
 // Vector steps over a 16-byte aligned run of n (a multiple of 8) logits.
-template <typename T, int LPR, int kUnroll>
+template <typename T, int LPR, int kUnroll, bool NT>
 __device__ inline void state_vec(const T *zt, const T *zs, int n, float c, int li, VState &s) {
     using Io = VIo<T>;
     const int nst = n / kStep;
@@ -229,8 +249,8 @@ __device__ inline void state_vec(const T *zt, const T *zs, int n, float c, int l
         typename Io::Raw a[kUnroll], b[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            a[u] = Io::load(zt + (int64_t)(k + u * LPR) * kStep);
-            b[u] = Io::load(zs + (int64_t)(k + u * LPR) * kStep);
+            a[u] = Io::template load<NT>(zt + (int64_t)(k + u * LPR) * kStep);
+            b[u] = Io::template load<NT>(zs + (int64_t)(k + u * LPR) * kStep);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -242,8 +262,8 @@ __device__ inline void state_vec(const T *zt, const T *zs, int n, float c, int l
     }
     for (; k < nst; k += LPR) {
         float x[8], y[8];
-        Io::widen(Io::load(zt + (int64_t)k * kStep), x);
-        Io::widen(Io::load(zs + (int64_t)k * kStep), y);
+        Io::widen(Io::template load<NT>(zt + (int64_t)k * kStep), x);
+        Io::widen(Io::template load<NT>(zs + (int64_t)k * kStep), y);
         vs_fold8(s, x, y, c);
     }
 }
@@ -256,11 +276,11 @@ __device__ inline void state_vec(const T *zt, const T *zs, int n, float c, int l
 // first boundary and lanes 8-15 the tail after the last whole step, one logit
 // each, and the aligned body is streamed as in the vector case; rows without
 // that match are read one logit per lane and step.
-template <typename T, bool VEC, int LPR, int kUnroll = kUnrollState>
+template <typename T, bool VEC, int LPR, bool NT, int kUnroll = kUnrollState>
 __device__ inline void row_state(const T *zt, const T *zs, int V, float c, int li, VState &s) {
     using Io = VIo<T>;
     if (VEC) {
-        state_vec<T, LPR, kUnroll>(zt, zs, V, c, li, s);
+        state_vec<T, LPR, kUnroll, NT>(zt, zs, V, c, li, s);
         return;
     }
     const int h = head_elems(zt);
@@ -275,7 +295,7 @@ __device__ inline void row_state(const T *zt, const T *zs, int V, float c, int l
         x[0] = v >= 0 ? Io::load1(zt + v) : kPad;
         y[0] = v >= 0 ? Io::load1(zs + v) : kPad;
         vs_fold8(s, x, y, c);
-        state_vec<T, LPR, kUnroll>(zt + h, zs + h, body, c, li, s);
+        state_vec<T, LPR, kUnroll, NT>(zt + h, zs + h, body, c, li, s);
         return;
     }
     for (int base = 0; base < V; base += kStep * LPR) {
@@ -348,7 +368,7 @@ __global__ __launch_bounds__(block_threads<WPR>()) void streamkl_vocab_fwd_kerne
     const T *zs = static_cast<const T *>(p.zs) + row * p.ld_s;
     VState s;
     vs_init(s);
-    row_state<T, VEC, LPR>(zt, zs, p.V, p.c, li, s);
+    row_state<T, VEC, LPR, true>(zt, zs, p.V, p.c, li, s);
     row_reduce<WPR>(s, p.c, red);
     if (li == 0) {
         const RowResult r = row_finish(s, p.c, p.scale);
@@ -395,7 +415,7 @@ __device__ inline GradRow grad_row(const VocabParams &p, int64_t row, float kl, 
 // multiple of 8) logits and the matching runs of the outputs.
 // REV: walk the steps from the end of the run (the fused launch's second
 // pass, so that it starts with the logits its first pass read last).
-template <typename T, bool TEACHER, int LPR, int kUnroll, bool REV = false>
+template <typename T, bool TEACHER, int LPR, int kUnroll, bool REV, bool NT>
 __device__ inline void grads_vec(const GradRow &r, float c, const T *zt, const T *zs, T *gs_out, T *gt_out, int n,
                                  int li) {
     using Io = VIo<T>;
@@ -406,8 +426,8 @@ __device__ inline void grads_vec(const GradRow &r, float c, const T *zt, const T
         typename Io::Raw a[kUnroll], b[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            a[u] = Io::load(zt + at(k + u * LPR));
-            b[u] = Io::load(zs + at(k + u * LPR));
+            a[u] = Io::template load<NT>(zt + at(k + u * LPR));
+            b[u] = Io::template load<NT>(zs + at(k + u * LPR));
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -415,24 +435,24 @@ __device__ inline void grads_vec(const GradRow &r, float c, const T *zt, const T
             Io::widen(a[u], x);
             Io::widen(b[u], y);
             grad8<TEACHER>(r, c, x, y, ds, dt);
-            Io::store(gs_out + at(k + u * LPR), ds);
-            if (TEACHER) Io::store(gt_out + at(k + u * LPR), dt);
+            Io::template store<NT>(gs_out + at(k + u * LPR), ds);
+            if (TEACHER) Io::template store<NT>(gt_out + at(k + u * LPR), dt);
         }
     }
     for (; k < nst; k += LPR) {
         float x[8], y[8], ds[8], dt[8];
-        Io::widen(Io::load(zt + at(k)), x);
-        Io::widen(Io::load(zs + at(k)), y);
+        Io::widen(Io::template load<NT>(zt + at(k)), x);
+        Io::widen(Io::template load<NT>(zs + at(k)), y);
         grad8<TEACHER>(r, c, x, y, ds, dt);
-        Io::store(gs_out + at(k), ds);
-        if (TEACHER) Io::store(gt_out + at(k), dt);
+        Io::template store<NT>(gs_out + at(k), ds);
+        if (TEACHER) Io::template store<NT>(gt_out + at(k), dt);
     }
 }
 
 // Gradient pass of one row, with the same three layouts as row_state (the
 // head/body/tail split also needs the output rows to start equally far from a
 // 16-byte boundary).
-template <typename T, bool VEC, bool TEACHER, int LPR, int kUnroll = unroll_grad<T>(), bool REV = false>
+template <typename T, bool VEC, bool TEACHER, int LPR, bool NT, int kUnroll = unroll_grad<T>(), bool REV = false>
 __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRow &r, int li) {
     using Io = VIo<T>;
     const T *zt = static_cast<const T *>(p.zt) + row * p.ld_t;
@@ -441,7 +461,7 @@ __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRo
     T *gt_out = TEACHER ? static_cast<T *>(p.dzt) + row * (int64_t)p.V : nullptr;
     const int V = p.V;
     if (VEC) {
-        grads_vec<T, TEACHER, LPR, kUnroll, REV>(r, p.c, zt, zs, gs_out, gt_out, V, li);
+        grads_vec<T, TEACHER, LPR, kUnroll, REV, NT>(r, p.c, zt, zs, gs_out, gt_out, V, li);
         return;
     }
     const int h = head_elems(zt);
@@ -460,7 +480,7 @@ __device__ inline void row_grads(const VocabParams &p, int64_t row, const GradRo
             Io::store1(gs_out + v, ds[0]);
             if (TEACHER) Io::store1(gt_out + v, dt[0]);
         }
-        grads_vec<T, TEACHER, LPR, kUnroll, REV>(r, p.c, zt + h, zs + h, gs_out + h, TEACHER ? gt_out + h : nullptr,
+        grads_vec<T, TEACHER, LPR, kUnroll, REV, NT>(r, p.c, zt + h, zs + h, gs_out + h, TEACHER ? gt_out + h : nullptr,
                                                  body, li);
         return;
     }
@@ -492,7 +512,7 @@ __global__ __launch_bounds__(block_threads<WPR>()) void streamkl_vocab_bwd_kerne
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     if (row >= p.rows) return;  // no barrier in this kernel
     const GradRow r = grad_row<TEACHER>(p, row, TEACHER ? p.kl[row] : 0.f, p.lse_t[row], p.lse_s[row]);
-    row_grads<T, VEC, TEACHER, LPR>(p, row, r, threadIdx.x % LPR);
+    row_grads<T, VEC, TEACHER, LPR, true>(p, row, r, threadIdx.x % LPR);
 }
 
 // ================================================================= fused forward + backward
@@ -511,7 +531,7 @@ __global__ __launch_bounds__(block_threads<WPR>()) void streamkl_vocab_fused_ker
     const T *zs = static_cast<const T *>(p.zs) + row * p.ld_s;
     VState s;
     vs_init(s);
-    row_state<T, VEC, LPR>(zt, zs, p.V, p.c, li, s);
+    row_state<T, VEC, LPR, false>(zt, zs, p.V, p.c, li, s);  // ordinary loads: the second pass re-reads the row
     row_reduce<WPR>(s, p.c, red);  // every lane of the row holds the row's state
     const RowResult r = row_finish(s, p.c, p.scale);
     if (li == 0) {
@@ -521,7 +541,7 @@ __global__ __launch_bounds__(block_threads<WPR>()) void streamkl_vocab_fused_ker
     }
     const GradRow gr = grad_row<TEACHER>(p, row, r.kl, r.lt, r.ls);
     // second pass from the end of the row: the logits read last are the likeliest still cached
-    row_grads<T, VEC, TEACHER, LPR, kUnrollState, true>(p, row, gr, li);
+    row_grads<T, VEC, TEACHER, LPR, true, kUnrollState, true>(p, row, gr, li);
 }
 
 // ================================================================= host side
