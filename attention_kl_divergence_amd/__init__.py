@@ -497,16 +497,41 @@ def _inputs_varlen(q_t, k_t, q_s, k_s, cu_q, cu_k, max_q, max_k):
     return (cu_q.numel() - 1, H, int(max_q), int(max_k), d_t, d_s), strides, (hq_t, hk_t, hq_s, hk_s)
 
 
+def check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, total_q=None, total_k=None):
+    """Host-side check of packed-sequence offsets (copies them to the host,
+    which synchronises the device): offsets start at 0 or above, never
+    decrease, stay within the packed rows, and no sequence is longer than its
+    max_seqlen.  The kernels themselves clamp a longer sequence to max_seqlen
+    (its extra rows are ignored), so a caller that cannot vouch for its
+    offsets should call this first."""
+    for name, cu, mx, total in (("cu_seqlens_q", cu_seqlens_q, max_seqlen_q, total_q),
+                                ("cu_seqlens_k", cu_seqlens_k, max_seqlen_k, total_k)):
+        c = [int(v) for v in cu.detach().cpu().tolist()]
+        if c[0] < 0:
+            raise ValueError(f"{name}: negative first offset {c[0]}")
+        lens = [b - a for a, b in zip(c[:-1], c[1:])]
+        if any(n < 0 for n in lens):
+            raise ValueError(f"{name}: offsets decrease")
+        if any(n > int(mx) for n in lens):
+            raise ValueError(f"{name}: a sequence of length {max(lens)} exceeds max_seqlen {int(mx)}")
+        if total is not None and c[-1] > total:
+            raise ValueError(f"{name}: last offset {c[-1]} past the {total} packed rows")
+
+
 def streamkl_fwd_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                        tau_t=None, tau_s=None, causal=False, with_sum=True):
+                        tau_t=None, tau_s=None, causal=False, with_sum=True, check_lengths=False):
     """Forward over packed sequences: q_* [total_q, heads, d], k_* [total_k,
     heads, d], batch b owning rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1.
     Returns (kl_rows, lse_t, lse_s, kl_sum) with the per-row outputs padded
-    to [B, H, max_seqlen_q] (rows past a sequence's length are 0)."""
+    to [B, H, max_seqlen_q] (rows past a sequence's length are 0).  A sequence
+    longer than its max_seqlen is cut to max_seqlen rows; check_lengths=True
+    runs check_cu_seqlens first (a device synchronisation)."""
     import torch
     lib = load_library()
     (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k,
                                                                  max_seqlen_q, max_seqlen_k)
+    if check_lengths:
+        check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, n_q, n_k, q_t.shape[0], k_t.shape[0])
     tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
     dev = q_t.device
     kl = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
@@ -523,15 +548,18 @@ def streamkl_fwd_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seql
 
 def streamkl_bwd_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, lse_t, lse_s,
                         grad_rows=None, grad_scalar=1.0, tau_t=None, tau_s=None, causal=False, teacher=False,
-                        kl_rows=None):
+                        kl_rows=None, check_lengths=False):
     """Backward over packed sequences: (dq, dk) packed like the inputs of the
     differentiated model (the student, or the teacher if teacher=True, which
     needs the forward's kl_rows).  Per-row arrays are [B, H, max_seqlen_q].
-    Only rows some sequence owns are written."""
+    The kernels write the rows some sequence owns; the outputs start zeroed,
+    so packed rows that no sequence owns get zero gradients."""
     import torch
     lib = load_library()
     (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k,
                                                                  max_seqlen_q, max_seqlen_k)
+    if check_lengths:
+        check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, n_q, n_k, q_t.shape[0], k_t.shape[0])
     tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
     dev = q_t.device
     rowargs = (("lse_t", lse_t), ("lse_s", lse_s)) + ((("kl_rows", kl_rows),) if teacher else ()) + \
@@ -540,11 +568,11 @@ def streamkl_bwd_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seql
         if t is None or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, n_q):
             raise ValueError(f"{name} must be a contiguous fp32 [B, H, max_seqlen_q] tensor")
     if teacher:
-        dq = torch.empty((q_t.shape[0], heads[0], d_t), dtype=q_t.dtype, device=dev)
-        dk = torch.empty((k_t.shape[0], heads[1], d_t), dtype=q_t.dtype, device=dev)
+        dq = torch.zeros((q_t.shape[0], heads[0], d_t), dtype=q_t.dtype, device=dev)
+        dk = torch.zeros((k_t.shape[0], heads[1], d_t), dtype=q_t.dtype, device=dev)
     else:
-        dq = torch.empty((q_s.shape[0], heads[2], d_s), dtype=q_s.dtype, device=dev)
-        dk = torch.empty((k_s.shape[0], heads[3], d_s), dtype=q_s.dtype, device=dev)
+        dq = torch.zeros((q_s.shape[0], heads[2], d_s), dtype=q_s.dtype, device=dev)
+        dk = torch.zeros((k_s.shape[0], heads[3], d_s), dtype=q_s.dtype, device=dev)
     lay = StreamKLLayout(*heads, None, None, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr())
     args = [q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(), _dtype_code(q_t), B, H, n_q, n_k, d_t,
             d_s, strides, ctypes.byref(lay), tau_t, tau_s, int(bool(causal)), lse_t.data_ptr(), lse_s.data_ptr()]
@@ -663,14 +691,17 @@ _vocab_fn_cache = None
 
 
 def attention_kl_varlen(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, tau_t=None,
-                        tau_s=None, causal=False):
+                        tau_s=None, causal=False, check_lengths=False):
     """Differentiable per-row attention KL over packed sequences ([rows, heads,
     d] tensors, int32 offsets [B + 1]); returns [B, H, max_seqlen_q], rows past
-    a sequence's length 0.  Rows of the packed gradients that no sequence owns
-    are left unwritten."""
+    a sequence's length 0.  Packed rows that no sequence owns get zero
+    gradients.  check_lengths=True checks the offsets on the host first (see
+    check_cu_seqlens)."""
     global _varlen_fn_cache
     if _varlen_fn_cache is None:
         _varlen_fn_cache = _varlen_autograd_function()
+    if check_lengths:
+        check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, q_t.shape[0], k_t.shape[0])
     return _varlen_fn_cache.apply(q_t, k_t, q_s, k_s, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q),
                                   int(max_seqlen_k), tau_t, tau_s, causal)
 
@@ -699,7 +730,8 @@ def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, seqle
 
 __all__ = [
     "streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
-    "attention_kl", "streamkl_fwd_varlen", "streamkl_bwd_varlen", "attention_kl_varlen", "streamkl_vocab_fwd",
+    "attention_kl", "streamkl_fwd_varlen", "streamkl_bwd_varlen", "attention_kl_varlen", "check_cu_seqlens",
+    "streamkl_vocab_fwd",
     "streamkl_vocab_bwd", "streamkl_vocab_fwd_bwd", "vocab_kl", "load_library", "supported", "status_string",
     "StreamKLError", "STREAMKL_F32", "STREAMKL_BF16"
 ]

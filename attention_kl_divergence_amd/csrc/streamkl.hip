@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
         const bool empty = !qv || L == 0.f;
         const int64_t row = ((int64_t)bb * p.H + hh) * p.n_q + q;
         if (p.state) {
-            float *o6 = p.state + ((int64_t)split * p.nheads * n_q + row) * kStateFloats;
+            float *o6 = p.state + ((int64_t)split * p.nheads * p.n_q + row) * kStateFloats;  // [n_split][B H n_q][6]
             o6[0] = empty ? kMasked : m;
             o6[1] = empty ? 0.f : L;
             o6[2] = empty ? 0.f : AT;

@@ -237,9 +237,13 @@ streamkl_status streamkl_bwd_teacher(const void *q_t, const void *k_t, const voi
  * Packed sequences: cu_seqlens_q (device int32 [B + 1], NULL = padded) makes
  * the queries packed: batch b owns query rows cu_seqlens_q[b] ..
  * cu_seqlens_q[b + 1] - 1 of q_t [rows, heads_q_t, d_t] and q_s [rows,
- * heads_q_s, d_s] (n_q is then the longest sequence; longer ones are cut to
- * it), and dq_s / dq_t come back packed the same way, contiguous, only the
- * valid rows written.  cu_seqlens_k does the same for the keys.  The batch
+ * heads_q_s, d_s] (n_q is then the longest sequence; a longer one is cut to
+ * its first n_q rows, without an error: the offsets live in device memory
+ * and are not read on the host), and dq_s / dq_t come back packed the same
+ * way, contiguous.  Only the rows some sequence owns are written: rows before
+ * cu_seqlens_q[0], past cu_seqlens_q[B], or past a cut sequence's n_q are
+ * left as the caller allocated them (the Python binding passes zeroed
+ * buffers, so they come back 0).  cu_seqlens_k does the same for the keys.  The batch
  * stride of a packed tensor is ignored (its rows are located by the
  * offsets); NULL strides mean contiguous [rows, heads, d].  A kind is either
  * packed or padded with lengths: seqlen_q together with cu_seqlens_q is

@@ -358,3 +358,63 @@ def test_packed_sequences_autograd():
     for got, ref in ((leaves[2].grad, ref_s[0]), (leaves[3].grad, ref_s[1]), (leaves[0].grad, ref_t[0]),
                      (leaves[1].grad, ref_t[1])):
         assert torch.equal(got, ref)
+
+
+def test_packed_rows_no_sequence_owns_get_zero_gradients():
+    """Packed buffers with rows before the first offset and after the last one
+    (owned by no sequence): those rows of both packed gradients are exactly 0
+    for student and teacher gradients, under autograd too, and the owned rows
+    match a launch on the trimmed buffers bit for bit."""
+    lq, lk = [40, 70], [60, 70]
+    lead, tail = 5, 9  # unowned rows before cu[0] and after cu[B]
+    cq = torch.tensor(np.concatenate([[lead], lead + np.cumsum(lq)]), dtype=torch.int32, device="cuda")
+    ck = torch.tensor(np.concatenate([[lead], lead + np.cumsum(lk)]), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(51)
+    tq, tk = lead + sum(lq) + tail, lead + sum(lk) + tail
+    mk = lambda n, h, d: torch.from_numpy(rng.standard_normal((n, h, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    q_t, k_t, q_s, k_s = mk(tq, 2, 64), mk(tk, 2, 64), mk(tq, 2, 64), mk(tk, 2, 64)
+    args = (q_t, k_t, q_s, k_s, cq, ck, max(lq), max(lk))
+    _, lt, ls, _ = skl.streamkl_fwd_varlen(*args)
+    kl = skl.streamkl_fwd_varlen(*args)[0]
+    dq, dk = skl.streamkl_bwd_varlen(*args, lt, ls)
+    tdq, tdk = skl.streamkl_bwd_varlen(*args, lt, ls, teacher=True, kl_rows=kl)
+    # the same sequences without the unowned rows
+    c0q = cq - lead
+    c0k = ck - lead
+    trim = (q_t[lead:lead + sum(lq)], k_t[lead:lead + sum(lk)], q_s[lead:lead + sum(lq)], k_s[lead:lead + sum(lk)])
+    targs = (*[t.contiguous() for t in trim], c0q, c0k, max(lq), max(lk))
+    _, lt0, ls0, _ = skl.streamkl_fwd_varlen(*targs)
+    rdq, rdk = skl.streamkl_bwd_varlen(*targs, lt0, ls0)
+    leaves = [t.clone().requires_grad_(True) for t in (q_t, k_t, q_s, k_s)]
+    skl.attention_kl_varlen(*leaves, cq, ck, max(lq), max(lk), check_lengths=True).sum().backward()
+    torch.cuda.synchronize()
+    for g_q, g_k in ((dq, dk), (tdq, tdk), (leaves[2].grad, leaves[3].grad), (leaves[0].grad, leaves[1].grad)):
+        for g, n in ((g_q, sum(lq)), (g_k, sum(lk))):
+            assert torch.count_nonzero(g[:lead]) == 0
+            assert torch.count_nonzero(g[lead + n:]) == 0
+            assert torch.count_nonzero(g[lead:lead + n]) > 0
+    assert torch.equal(dq[lead:lead + sum(lq)], rdq)
+    assert torch.equal(dk[lead:lead + sum(lk)], rdk)
+
+
+def test_packed_offsets_checked_on_request():
+    """check_lengths=True rejects a sequence longer than max_seqlen, decreasing
+    offsets and offsets past the packed rows; without it the kernels cut the
+    long sequence to max_seqlen rows (documented behaviour)."""
+    lq = [30, 50]
+    cq = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(52)
+    mk = lambda n: torch.from_numpy(rng.standard_normal((n, 1, 64), dtype=np.float32)).cuda()
+    x = (mk(80), mk(80), mk(80), mk(80))
+    with pytest.raises(ValueError, match="exceeds max_seqlen"):
+        skl.streamkl_fwd_varlen(*x, cq, cq, 40, 40, check_lengths=True)
+    with pytest.raises(ValueError, match="decrease"):
+        bad = torch.tensor([0, 50, 30], dtype=torch.int32, device="cuda")
+        skl.streamkl_fwd_varlen(*x, bad, bad, 50, 50, check_lengths=True)
+    with pytest.raises(ValueError, match="past the"):
+        far = torch.tensor([0, 30, 90], dtype=torch.int32, device="cuda")
+        skl.streamkl_fwd_varlen(*x, far, far, 60, 60, check_lengths=True)
+    kl, _, _, _ = skl.streamkl_fwd_varlen(*x, cq, cq, 50, 50, check_lengths=True)
+    cut, _, _, _ = skl.streamkl_fwd_varlen(*x, cq, cq, 40, 40)
+    torch.cuda.synchronize()
+    assert kl.shape == (2, 1, 50) and cut.shape == (2, 1, 40)

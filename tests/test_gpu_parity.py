@@ -130,10 +130,13 @@ def test_identical_teacher_and_student_give_zero(dtype):
     w = W["corr_4k"].resized(B=2, H=2, n_q=150, n_k=170, dtype=dtype, seed=208)
     x = inputs.make(w)
     x["q_s"], x["k_s"] = x["q_t"], x["k_t"]
+    assert w.tau_t == w.tau_s
     out = _gpu(w, x)
-    assert np.max(np.abs(out["kl"])) <= 1e-5
-    assert np.max(np.abs(out["dq"])) <= 1e-6 and np.max(np.abs(out["dk"])) <= 1e-6
-    np.testing.assert_allclose(out["lse_t"], out["lse_s"], rtol=0, atol=1e-6)
+    # KL = 0 iff the two distributions are equal: the teacher and student
+    # paths see the same bits, so every difference is exactly 0
+    assert np.all(out["kl"] == 0.0) and out["sum"] == 0.0
+    assert np.all(out["dq"] == 0.0) and np.all(out["dk"] == 0.0)
+    np.testing.assert_array_equal(out["lse_t"], out["lse_s"])
 
 
 def test_strided_views_match_contiguous():
@@ -243,7 +246,10 @@ def test_autograd_function_and_extra_memory():
 
 # ------------------------------------------------------------------ full sizes
 FULL = ["corr_4k", "causal_32k", "mixed_dims_2k", "cross_512x16k", "corr_16k"]
-DK_FULL = {"corr_4k", "mixed_dims_2k", "cross_512x16k"}  # whole-head dk oracle is affordable
+# dK_s rows checked against the oracle on one whole head (oracle.dk_keys: the
+# head's full score rows in fp64, about 137 GFLOP at 16K x 16K and 275 GFLOP
+# at the 32K causal size, seconds on the host's cores)
+DK_FULL = set(FULL)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -257,7 +263,7 @@ def test_full_size_sampled_parity(name):
     rng = np.random.default_rng(w.seed + 7)
     n_rows = w.B * w.H * w.n_q
     heads = [(0, 0), (w.B - 1, w.H - 1)]
-    rows = set(rng.choice(n_rows, 40, replace=False).tolist())
+    rows = set(rng.choice(n_rows, 400, replace=False).tolist())
     for b, h in heads:
         base = (b * w.H + h) * w.n_q
         rows |= {base, base + 1, base + w.n_q // 2, base + w.n_q - 1}
@@ -269,12 +275,16 @@ def test_full_size_sampled_parity(name):
     check_lse(out["lse_s"].ravel()[rows], ls, w.dtype, "lse_s")
     # the reduced scalar against the rows the GPU produced
     assert abs(out["sum"] - float(np.sum(out["kl"], dtype=np.float64))) <= 1e-6 * float(np.sum(np.abs(out["kl"])))
-    qrows = rows[:: max(1, rows.size // 16)]
+    qrows = rows[:: max(1, rows.size // 64)]
     dq = oracle.dq_rows(xo["q_t"], xo["k_t"], xo["q_s"], xo["k_s"], w.tau_t, w.tau_s, w.causal, qrows)
     check_grad(out["dq"].reshape(-1, w.d_s)[qrows], dq, w.dtype, "dq_s rows")
     if name in DK_FULL:
         b, h = heads[-1]
-        keys = np.array(sorted(set(rng.choice(w.n_k, 6, replace=False).tolist()) | {0, w.n_k - 1}), dtype=np.int64)
+        # keys near both ends, six at random and one interior 32-key tile
+        mid = (w.n_k // 2 // 32) * 32
+        keys = set(rng.choice(w.n_k, 6, replace=False).tolist()) | {0, 1, w.n_k - 2, w.n_k - 1}
+        keys |= set(range(mid, min(w.n_k, mid + 32), 5))
+        keys = np.array(sorted(keys), dtype=np.int64)
         print(f"[full] {name}: oracle dk on head {(b, h)}", flush=True)
         dk = oracle.dk_keys(xo["q_t"], xo["k_t"], xo["q_s"], xo["k_s"], w.tau_t, w.tau_s, w.causal, b, h, keys)
         check_grad(out["dk"][b, h][keys], dk, w.dtype, "dk_s keys")
