@@ -73,6 +73,9 @@ def load_library():
     lib.streamkl_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, i, vp, sz, vp, vp, vp,
                                        vp, vp]
     lib.streamkl_fwd_split.restype = i
+    lib.streamkl_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, f, f, i, i, vp, vp, vp,
+                                               vp, vp]
+    lib.streamkl_fwd_split_noalloc.restype = i
     lay = ctypes.POINTER(StreamKLLayout)
     lib.streamkl_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i64p, lay, f, f, i, vp, vp, vp, vp, vp]
     lib.streamkl_fwd_ex.restype = i
@@ -236,6 +239,40 @@ def streamkl_fwd(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, with_
                             tot.data_ptr() if tot is not None else None, _stream_ptr(dev))
     _check("streamkl_fwd", code)
     return kl, lt, ls, tot
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # STREAMKL_NOALLOC_SCRATCH_BYTES
+
+
+def streamkl_fwd_noalloc(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, split=None, kl=None, lse_t=None,
+                         lse_s=None, kl_sum=None):
+    """The split forward through streamkl_fwd_split_noalloc, whose split states
+    live in the library's per-GPU scratch array: no device memory is allocated
+    for them.  Pass preallocated fp32 outputs (kl, lse_t, lse_s [B, H, N_Q],
+    kl_sum [1] or None) to allocate nothing at all; missing ones are
+    allocated here.  Calls that overlap on one GPU race (see the header)."""
+    import torch
+    lib = load_library()
+    (B, H, n_q, n_k, d_t, d_s), strides, heads = _inputs(q_t, k_t, q_s, k_s)
+    if any(h != H for h in heads):
+        raise ValueError("streamkl_fwd_noalloc takes equal head counts")
+    tau_t, tau_s = _taus(tau_t, tau_s, d_t, d_s)
+    dev = q_t.device
+    n_split = int(lib.streamkl_fwd_split_count(B, H, n_q, n_k, int(bool(causal)))) if split is None else int(split)
+    outs = []
+    for t in (kl, lse_t, lse_s):
+        if t is None:
+            t = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
+        elif t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, n_q) or t.device != dev:
+            raise ValueError("kl, lse_t and lse_s must be contiguous fp32 [B, H, N_Q] tensors on the inputs' device")
+        outs.append(t)
+    code = lib.streamkl_fwd_split_noalloc(q_t.data_ptr(), k_t.data_ptr(), q_s.data_ptr(), k_s.data_ptr(),
+                                          _dtype_code(q_t), B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s,
+                                          int(bool(causal)), n_split, outs[0].data_ptr(), outs[1].data_ptr(),
+                                          outs[2].data_ptr(), kl_sum.data_ptr() if kl_sum is not None else None,
+                                          _stream_ptr(dev))
+    _check("streamkl_fwd_split_noalloc", code)
+    return outs[0], outs[1], outs[2], kl_sum
 
 
 STATE_FLOATS = 6
@@ -729,7 +766,7 @@ def attention_kl(q_t, k_t, q_s, k_s, tau_t=None, tau_s=None, causal=False, seqle
 
 
 __all__ = [
-    "streamkl_fwd", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
+    "streamkl_fwd", "streamkl_fwd_noalloc", "streamkl_fwd_partial", "streamkl_fwd_merge", "streamkl_bwd", "streamkl_bwd_teacher",
     "attention_kl", "streamkl_fwd_varlen", "streamkl_bwd_varlen", "attention_kl_varlen", "check_cu_seqlens",
     "streamkl_vocab_fwd",
     "streamkl_vocab_bwd", "streamkl_vocab_fwd_bwd", "vocab_kl", "load_library", "supported", "status_string",

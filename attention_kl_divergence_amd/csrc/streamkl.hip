@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <math.h>
 #include <stdint.h>
@@ -1181,6 +1182,20 @@ __global__ __launch_bounds__(256) void streamkl_split_reduce_kernel(const float 
     }
 }
 
+}  // namespace
+
+// Scratch of the allocation-free split forward: the split states live in
+// this file-scope array (external linkage, so that the device code keeps it
+// although no kernel names it).  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a stand-in, not a device address): the
+// device address of each GPU's copy comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and is kept per device.
+namespace streamkl_internal {
+__device__ __align__(256) unsigned char scratch[STREAMKL_NOALLOC_SCRATCH_BYTES];
+}
+
+namespace {
+
 // ================================================================= host side
 struct Shape {
     int B, H, n_q, n_k, d_t, d_s;
@@ -1552,6 +1567,23 @@ size_t bwd_ex_workspace(int B, int H, int n_q, int n_k, int d_t, int d_s, const 
     return need;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (null on failure).
+void *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(streamkl_internal::scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -1624,6 +1656,36 @@ streamkl_status streamkl_fwd_split(const void *q_t, const void *k_t, const void 
     if (rc != STREAMKL_OK) return rc;
     return streamkl_fwd_merge(state, n_split, (int64_t)B * H * n_q, tau_t, tau_s, kl_rows, lse_t, lse_s, kl_sum,
                               stream);
+}
+
+streamkl_status streamkl_fwd_split_noalloc(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                           streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                           const int64_t *strides, float tau_t, float tau_s, int causal,
+                                           int n_split, float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
+                                           void *stream) {
+    if (!kl_rows || !lse_t || !lse_s) return STREAMKL_ERR_INVALID;
+    if (n_split < 1 || n_split > kMaxSplit) return STREAMKL_ERR_INVALID;
+    if (B < 1 || H < 1 || n_q < 1) return STREAMKL_ERR_INVALID;
+    if (n_split == 1)  // one key range: no states, nothing to hold
+        return fwd_common(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, nullptr, tau_t, tau_s,
+                          causal, 0, n_k, 1, nullptr, kl_rows, lse_t, lse_s, kl_sum, stream);
+    {
+        // the argument checks of the split forward, on the host, before any HIP call
+        Heads hd;
+        resolve_layout(nullptr, H, hd);
+        int64_t st[12];
+        const streamkl_status rc = check_common(q_t, k_t, q_s, k_s, dtype, Shape{B, H, n_q, n_k, d_t, d_s},
+                                                strides, tau_t, tau_s, causal, hd, st);
+        if (rc != STREAMKL_OK) return rc;
+    }
+    if (streamkl_fwd_split_workspace_size(B, H, n_q, n_split) > STREAMKL_NOALLOC_SCRATCH_BYTES)
+        return STREAMKL_ERR_WORKSPACE;
+    void *ws = scratch_on_current_device();
+    if (!ws) return STREAMKL_ERR_HIP;
+    // every (split, row) state is written by the partial launch before the
+    // merge reads it, so the array needs no clearing between calls
+    return streamkl_fwd_split(q_t, k_t, q_s, k_s, dtype, B, H, n_q, n_k, d_t, d_s, strides, tau_t, tau_s, causal,
+                              n_split, ws, STREAMKL_NOALLOC_SCRATCH_BYTES, kl_rows, lse_t, lse_s, kl_sum, stream);
 }
 
 streamkl_status streamkl_fwd_partial(const void *q_t, const void *k_t, const void *q_s, const void *k_s,

@@ -148,6 +148,26 @@ streamkl_status streamkl_fwd_split(const void *q_t, const void *k_t, const void 
                                    void *workspace, size_t workspace_bytes, float *kl_rows, float *lse_t,
                                    float *lse_s, float *kl_sum, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * streamkl_fwd_split with the split states in a scratch array the library
+ * holds on each GPU it runs on (STREAMKL_NOALLOC_SCRATCH_BYTES, a fixed
+ * 16 MiB per GPU, kept until the process ends) instead of a caller workspace.
+ * It allocates and frees nothing.  Arguments, outputs and errors as in
+ * streamkl_fwd_split, except that STREAMKL_ERR_WORKSPACE means the states
+ * (streamkl_fwd_split_workspace_size) would not fit in the scratch array, and
+ * STREAMKL_ERR_HIP also covers a failure to locate the array on the current
+ * device (the device the stream belongs to must be the current one).  Every
+ * call on one GPU uses that GPU's single array: calls that overlap on one GPU
+ * (on different streams, or from several host threads) race and must be
+ * serialised by the caller; consecutive calls on one stream are safe. */
+#define STREAMKL_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+streamkl_status streamkl_fwd_split_noalloc(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
+                                           streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
+                                           const int64_t *strides, float tau_t, float tau_s, int causal,
+                                           int n_split, float *kl_rows, float *lse_t, float *lse_s, float *kl_sum,
+                                           void *stream);
+
 /*
  * Backward.  Gradients of L = sum_r g_r KL_r with respect to the student
  * queries and keys; the teacher is a fixed target and gets no gradient.  The

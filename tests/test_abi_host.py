@@ -276,3 +276,22 @@ def test_packed_sequence_layout_is_validated_before_any_hip_call():
     assert fwd(ck=A + 6) == INV
     assert fwd(sq=A, cq=A + 64) == INV          # a kind cannot be both padded with lengths and packed
     assert fwd(sk=A, ck=A + 64) == INV
+
+
+def test_noalloc_split_forward_rejects_on_the_host():
+    """streamkl_fwd_split_noalloc: states past its fixed scratch array give
+    STREAMKL_ERR_WORKSPACE, and bad arguments INVALID, before any HIP call."""
+    lib = skl.load_library()
+    big = (64, 16, 4096, 8)  # 768 MiB of split states
+    assert lib.streamkl_fwd_split_workspace_size(big[0], big[1], big[2], big[3]) > skl.NOALLOC_SCRATCH_BYTES
+
+    def call(B, H, n_q, n_split, q_t=A, kl=A + 0x400000, tau=0.088):
+        return lib.streamkl_fwd_split_noalloc(q_t, A + 0x100000, A + 0x200000, A + 0x300000, skl.STREAMKL_BF16, B, H,
+                                              n_q, 8192, 128, 128, None, tau, tau, 0, n_split, kl, A + 0x500000,
+                                              A + 0x600000, None, None)
+    assert call(*big) == skl.STREAMKL_ERR_WORKSPACE
+    assert call(2, 2, 64, 2, q_t=None) == INV
+    assert call(2, 2, 64, 2, kl=None) == INV
+    assert call(2, 2, 64, 0) == INV
+    assert call(2, 2, 64, 65) == INV
+    assert call(2, 2, 64, 2, tau=-1.0) == INV
