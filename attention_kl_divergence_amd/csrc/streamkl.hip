@@ -910,27 +910,39 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     const float tau_g = FIRST ? p.tau_t : p.tau_s;  // the scale of the differentiated scores
     const float w_all = p.g_scalar * tau_g;
     const float lw_all = log2f(fabsf(w_all));
-    float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;  // dk mode: row values of query y0 + tid (tid < kBwdRows)
+    // dk mode: the raw per-query values of query y0 + tid (tid < kBwdRows),
+    // loaded before the stage's tile loads and turned into row values only
+    // when they are stored, at the end of the stage: their wait then covers
+    // them alone, not the tile loads issued after them
+    float lt_r = 0.f, ls_r = 0.f, kl_r = 0.f, g_r = 0.f;
+    bool y_ok = false;
     auto load_rows = [&](int st) {
         if (DKMODE && tid < kBwdRows) {
             const int y = ystart + st * kBwdRows + tid;
-            rv0 = rv1 = rv2 = 0.f;
-            if (y < n_q) {
-                rv0 = -p.lse_t[rowbase + y] * kLog2e;
-                if (FIRST) rv1 = -(p.lse_t[rowbase + y] - p.lse_s[rowbase + y] + p.kl[rowbase + y]);
-                else rv1 = -p.lse_s[rowbase + y] * kLog2e;
-                if (FOLD) {
-                    rv0 += lw_all;
-                    if (!FIRST) rv1 += lw_all;
-                } else {
-                    // per-row weight; the teacher kernels also take this path with a scalar g
-                    rv2 = (p.g ? p.g[rowbase + y] : p.g_scalar) * tau_g;
-                }
+            y_ok = y < n_q;
+            if (y_ok) {
+                lt_r = p.lse_t[rowbase + y];
+                ls_r = p.lse_s[rowbase + y];
+                if (FIRST) kl_r = p.kl[rowbase + y];
+                // per-row weight; the teacher kernels also take this path with a scalar g
+                if (!FOLD) g_r = p.g ? p.g[rowbase + y] : p.g_scalar;
             }
         }
     };
     auto store_rows = [&](int stage) {
         if (DKMODE && tid < kBwdRows) {
+            float rv0 = 0.f, rv1 = 0.f, rv2 = 0.f;
+            if (y_ok) {
+                rv0 = -lt_r * kLog2e;
+                if (FIRST) rv1 = -(lt_r - ls_r + kl_r);
+                else rv1 = -ls_r * kLog2e;
+                if (FOLD) {
+                    rv0 += lw_all;
+                    if (!FIRST) rv1 += lw_all;
+                } else {
+                    rv2 = g_r * tau_g;
+                }
+            }
             rowv[stage][0][tid] = rv0;
             rowv[stage][1][tid] = rv1;
             if (!FOLD) rowv[stage][2][tid] = rv2;
@@ -951,8 +963,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     // change of sign between heads negates it.
     auto begin_head = [&](int hh, bool first_head) {
         set_head(hh);
-        issue(0, 0);
         load_rows(0);
+        issue(0, 0);
         load_span_global<T, DT>(Xt + (int64_t)xc * sxt, hf, xv, xtv);
         load_span_global<T, DS>(Xs + (int64_t)xc * sxs, hf, xv, xsv);
         if (!DKMODE && xv) {
@@ -1016,8 +1028,8 @@ __device__ __attribute__((always_inline)) inline void bwd_block(const BwdParams 
     auto stage_body = [&](int st, auto plain_tag, int sc) {  // sc = st % 2, the ring slot
         constexpr bool PLAIN = decltype(plain_tag)::value;
         if (st + 1 < nstage) {
-            issue(st + 1, sc ^ 1);
             load_rows(st + 1);
+            issue(st + 1, sc ^ 1);
         }
 #pragma unroll
         for (int sub = 0; sub < kBwdSub; ++sub) {
