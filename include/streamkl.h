@@ -183,7 +183,13 @@ streamkl_status streamkl_fwd_split_noalloc(const void *q_t, const void *k_t, con
  *
  * No workspace is used: one deterministic launch, with no atomics, holds both a
  * query-major block per 128 queries (dq_s) and a key-major block per 128 keys
- * (dk_s) of every head.
+ * (dk_s) of every head.  The query-major blocks recompute the scores, so no
+ * dq_s partial sums cross blocks.  The alternative, key-major blocks only with
+ * dq_s summed by fp32 atomics into a caller workspace, would need one atomic
+ * add per query row, head-dimension element and 128-key block: 34 GB at
+ * B=2, H=16, n_q=n_k=16384, d=128, which on MI355X takes about 25 ms on its
+ * own, twice this whole backward.  So the call has no workspace arguments, and
+ * streamkl_bwd_workspace_size (below) returns 0 for every shape.
  */
 streamkl_status streamkl_bwd(const void *q_t, const void *k_t, const void *q_s, const void *k_s,
                              streamkl_dtype dtype, int B, int H, int n_q, int n_k, int d_t, int d_s,
