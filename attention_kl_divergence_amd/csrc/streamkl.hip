@@ -64,8 +64,10 @@ constexpr float kMasked = -1.0e30f;
 #endif
 constexpr int kWaves = STREAMKL_WAVES;  // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-// workgroups per CU the bf16 kernels are built for: two waves per SIMD
+// workgroups per CU the bf16 backward is built for: two waves per SIMD
 constexpr int kBf16Blocks = 8 / kWaves;
+// waves per SIMD the bf16 forward is built for (at most 168 registers each)
+constexpr int kBf16FwdWaves = 3;
 constexpr int kTile = 32;      // MFMA tile edge; each wave owns 32 stationary items
 constexpr int kBlockX = kWaves * kTile;
 constexpr int kBN = 32;        // streamed rows per pipeline stage
@@ -304,8 +306,6 @@ __device__ inline void batch_rows(const int *cu, const int *len, int b, int n, i
     }
 }
 
-// Scheduler group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 // C[y][x] = Y . X^T for one 32-row tile Y in LDS (pitch P) and this wave's
 // stationary fragments X.
@@ -412,11 +412,14 @@ __device__ inline void online_step(Online &o, const f32x16 &xt, const f32x16 &xs
 }
 
 // One block = kWaves waves x 32 queries.  The key tiles stream through a two-stage
-// LDS ring filled by direct buffer->LDS loads; in steady state the MFMAs of
-// tile j+1 are issued interleaved with the exponentials and sums of tile j
-// (which only need registers) while the loads of tile j+2 are in flight.
+// LDS ring filled by direct buffer->LDS loads: a wave scores tile j and folds
+// it into its running sums while the loads of tile j + 1 are in flight.  With
+// one score tile live per wave (about 160 registers) three waves share each
+// SIMD (bf16): while one waits for its MFMAs the others run exponentials.
+// This beat a two-deep pipeline at two waves per SIMD (the MFMAs of tile j + 1
+// interleaved with the sums of tile j), 4.84 -> 4.71 ms at 16384 x 16384.
 template <typename T, int DT, int DS, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void streamkl_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16FwdWaves : 1) void streamkl_fwd_kernel(FwdParams p) {
     using TileT = Tile<T, DT>;
     using TileS = Tile<T, DS>;
     constexpr int STAGE = TileT::kBytes + TileS::kBytes;
@@ -471,7 +474,6 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     };
 
     if (ntile > 0) issue(0, smem);
-    if (ntile > 1) issue(1, smem + STAGE);
 
     u32x4 qtv[span_vecs<T, DT>()], qsv[span_vecs<T, DS>()];
     load_span_global<T, DT>(Qt + (int64_t)qc * sqt, hf, qv, qtv);
@@ -481,50 +483,18 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16Blocks : 1) void st
     Online o{kMasked, 0.f, 0.f, 0.f, kMasked, 0.f};
 
     dma_barrier();
-    f32x16 xt0 = {}, xs0 = {}, xt1 = {}, xs1 = {};
-    if (ntile > 0 && active(0)) {
-        xt0 = tile_scores<T, DT>(smem, qtv, l32, hf);
-        xs0 = tile_scores<T, DS>(smem + TileT::kBytes, qsv, l32, hf);
-    }
-    dma_barrier();  // every wave is done with stage 0 before tile 2 lands there
-
-    // softmax of tile `it` (registers cur_*) + scores of tile it+1 (into nxt_*)
-    auto step = [&](int it, f32x16 &cur_t, f32x16 &cur_s, f32x16 &nxt_t, f32x16 &nxt_s) {
-        if (it + 2 < ntile) issue(it + 2, smem + (it & 1) * STAGE);
-        const bool a_cur = active(it);
-        const bool a_nxt = it + 1 < ntile && active(it + 1);
-        const bool m_cur = need_mask(it);
-        const char *bn = smem + ((it + 1) & 1) * STAGE;
-        const int k0 = (t0 + it) * kBN;
-        if (a_cur && a_nxt && !m_cur) {
-            nxt_t = tile_scores<T, DT>(bn, qtv, l32, hf);
-            nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, qsv, l32, hf);
-            online_step<CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
-            if constexpr (sizeof(T) == 2) {
-                constexpr int NM = Ty<T>::ksteps(DT) + Ty<T>::ksteps(DS);
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NM, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedValu, 12, 0);
-#pragma unroll
-                for (int k = 0; k < NM; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 9, 0);
-                }
-            }
-        } else {
-            if (a_nxt) {
-                nxt_t = tile_scores<T, DT>(bn, qtv, l32, hf);
-                nxt_s = tile_scores<T, DS>(bn + TileT::kBytes, qsv, l32, hf);
-            }
-            if (a_cur) {
-                if (m_cur) online_update<true, CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
-                else online_step<CAUSAL>(o, cur_t, cur_s, ct, cs, k0, hf, q, n_k, off);
-            }
+    for (int it = 0; it < ntile; ++it) {
+        // the other stage was read in the previous step: load tile it + 1 there
+        if (it + 1 < ntile) issue(it + 1, smem + ((it + 1) & 1) * STAGE);
+        const char *bc = smem + (it & 1) * STAGE;
+        if (active(it)) {
+            const int k0 = (t0 + it) * kBN;
+            const f32x16 xt = tile_scores<T, DT>(bc, qtv, l32, hf);
+            const f32x16 xs = tile_scores<T, DS>(bc + TileT::kBytes, qsv, l32, hf);
+            if (need_mask(it)) online_update<true, CAUSAL>(o, xt, xs, ct, cs, k0, hf, q, n_k, off);
+            else online_step<CAUSAL>(o, xt, xs, ct, cs, k0, hf, q, n_k, off);
         }
-        dma_barrier();  // publishes tile it + 2 for the next step's scores
-    };
-    for (int it = 0; it < ntile; it += 2) {
-        step(it, xt0, xs0, xt1, xs1);
-        if (it + 1 < ntile) step(it + 1, xt1, xs1, xt0, xs0);
+        dma_barrier();  // tile it + 1 is in LDS and every wave is done with tile it
     }
 
     // merge the two half-waves (same query, disjoint key subsets)
@@ -1633,11 +1603,18 @@ streamkl_status streamkl_fwd(const void *q_t, const void *k_t, const void *q_s, 
 }
 
 int streamkl_fwd_split_count(int B, int H, int n_q, int n_k, int causal) {
-    (void)causal;
     if (B < 1 || H < 1 || n_q < 1 || n_k < 1) return 1;
-    // aim at two workgroups per CU twice over (256 CUs); keep >= 16 key tiles per split
+    // One round of the bf16 forward is 256 CUs x 3 workgroups.  A launch that
+    // fills whole rounds, or about three, needs no split.  A smaller launch is
+    // split over the keys until it holds about 2048 blocks, keeping at least
+    // 16 key tiles per split; measured best at 2 x 16 heads of 4096 x 4096 and
+    // 8 x 16 heads of 512 queries x 16384 keys.  Under a causal mask the splits
+    // are uneven (early query blocks need few keys), so a causal launch is
+    // split only when it does not fill one round.
     const int64_t base = (int64_t)B * H * ((n_q + kBlockX - 1) / kBlockX);
-    const int64_t want = 2 * 2 * 256;
+    const int64_t round = 256 * kBf16FwdWaves;
+    if (base % round == 0) return 1;
+    const int64_t want = causal ? round : 2048;
     if (base >= want) return 1;
     int64_t n = (want + base - 1) / base;
     n = std::min<int64_t>(n, std::max<int64_t>(1, n_k / (16 * kBN)));

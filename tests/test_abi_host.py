@@ -166,9 +166,15 @@ def test_split_forward_pieces_reject_bad_arguments_before_any_hip_call():
     assert lib.streamkl_fwd_merge(None, 2, 100, 0.1, 0.1, A, A, A, None, None) == INV
     assert lib.streamkl_fwd_merge(A, 0, 100, 0.1, 0.1, A, A, A, None, None) == INV
     assert lib.streamkl_fwd_merge(A, 2, 0, 0.1, 0.1, A, A, A, None, None) == INV
-    # the suggested split count: 1 when the unsplit forward fills the GPU, more for small launches
+    # the suggested split count: 1 when the unsplit forward fills the GPU (or
+    # exactly fills whole rounds of 768 workgroups), more for small launches,
+    # never below 16 key tiles per split; causal launches only below one round
     assert lib.streamkl_fwd_split_count(2, 16, 16384, 16384, 0) == 1
-    assert lib.streamkl_fwd_split_count(4, 12, 2048, 2048, 0) == 2
+    assert lib.streamkl_fwd_split_count(4, 12, 2048, 2048, 0) == 1  # 768 blocks: one full round
+    assert lib.streamkl_fwd_split_count(2, 16, 4096, 4096, 0) == 2
+    assert lib.streamkl_fwd_split_count(8, 16, 512, 16384, 0) == 4
+    assert lib.streamkl_fwd_split_count(1, 8, 32768, 32768, 1) == 1
+    assert lib.streamkl_fwd_split_count(1, 2, 4096, 4096, 1) == 8  # 64 blocks, causal
     assert lib.streamkl_fwd_split_count(1, 1, 128, 128, 0) == 1
 
 

@@ -80,7 +80,7 @@ def test_backward_on_split_forward_statistics():
     check_grad(dk.float().cpu().numpy(), rdk, w.dtype, "dk_s")
 
 
-@pytest.mark.parametrize("name", ["mixed_dims_2k", "cross_512x16k"])
+@pytest.mark.parametrize("name", ["corr_4k", "cross_512x16k"])
 def test_auto_split_full_size_sampled(name):
     """The full workloads the split is suggested for, on sampled oracle rows."""
     w = W[name]
