@@ -263,7 +263,7 @@ def test_full_size_sampled_parity(name):
     rng = np.random.default_rng(w.seed + 7)
     n_rows = w.B * w.H * w.n_q
     heads = [(0, 0), (w.B - 1, w.H - 1)]
-    rows = set(rng.choice(n_rows, 400, replace=False).tolist())
+    rows = set(rng.choice(n_rows, min(n_rows, 2000), replace=False).tolist())
     for b, h in heads:
         base = (b * w.H + h) * w.n_q
         rows |= {base, base + 1, base + w.n_q // 2, base + w.n_q - 1}
@@ -275,19 +275,19 @@ def test_full_size_sampled_parity(name):
     check_lse(out["lse_s"].ravel()[rows], ls, w.dtype, "lse_s")
     # the reduced scalar against the rows the GPU produced
     assert abs(out["sum"] - float(np.sum(out["kl"], dtype=np.float64))) <= 1e-6 * float(np.sum(np.abs(out["kl"])))
-    qrows = rows[:: max(1, rows.size // 64)]
+    qrows = rows[:: max(1, rows.size // 256)]
     dq = oracle.dq_rows(xo["q_t"], xo["k_t"], xo["q_s"], xo["k_s"], w.tau_t, w.tau_s, w.causal, qrows)
     check_grad(out["dq"].reshape(-1, w.d_s)[qrows], dq, w.dtype, "dq_s rows")
     if name in DK_FULL:
-        b, h = heads[-1]
-        # keys near both ends, six at random and one interior 32-key tile
-        mid = (w.n_k // 2 // 32) * 32
-        keys = set(rng.choice(w.n_k, 6, replace=False).tolist()) | {0, 1, w.n_k - 2, w.n_k - 1}
-        keys |= set(range(mid, min(w.n_k, mid + 32), 5))
-        keys = np.array(sorted(keys), dtype=np.int64)
-        print(f"[full] {name}: oracle dk on head {(b, h)}", flush=True)
-        dk = oracle.dk_keys(xo["q_t"], xo["k_t"], xo["q_s"], xo["k_s"], w.tau_t, w.tau_s, w.causal, b, h, keys)
-        check_grad(out["dk"][b, h][keys], dk, w.dtype, "dk_s keys")
+        for b, h in heads:
+            # keys near both ends, six at random and one interior 32-key tile
+            mid = (w.n_k // 2 // 32) * 32
+            keys = set(rng.choice(w.n_k, 6, replace=False).tolist()) | {0, 1, w.n_k - 2, w.n_k - 1}
+            keys |= set(range(mid, min(w.n_k, mid + 32), 5))
+            keys = np.array(sorted(keys), dtype=np.int64)
+            print(f"[full] {name}: oracle dk on head {(b, h)}", flush=True)
+            dk = oracle.dk_keys(xo["q_t"], xo["k_t"], xo["q_s"], xo["k_s"], w.tau_t, w.tau_s, w.causal, b, h, keys)
+            check_grad(out["dk"][b, h][keys], dk, w.dtype, "dk_s keys")
     # identities that hold at any size: sum_j dK_s[j] = 0 and <Q_s,dQ_s> = <K_s,dK_s> per head
     dkf = out["dk"].astype(np.float64)
     dqf = out["dq"].astype(np.float64)
