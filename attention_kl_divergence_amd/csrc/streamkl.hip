@@ -568,13 +568,32 @@ __global__ __launch_bounds__(256) void streamkl_merge_kernel(const float *st, in
 }
 
 // Deterministic sum of n fp32 values, one block: each thread accumulates a
-// fixed, strided subset in fp64 with several loads in flight, then a fixed
-// tree combines the partial sums.
+// fixed, strided subset in fp64 with several loads in flight (16-byte loads
+// when x is 16-byte aligned), then a fixed tree combines the partial sums.
 __global__ __launch_bounds__(1024) void streamkl_sum_kernel(const float *x, int64_t n, float *out) {
     __shared__ double red[1024];
-    constexpr int U = 8;
     double s = 0.0;
-    int64_t i = threadIdx.x;
+    int64_t i0 = 0;  // first element left to the scalar loop
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        constexpr int U = 8;
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+        const int64_t n4 = n / 4;
+        int64_t j = threadIdx.x;
+        for (; j + (U - 1) * 1024 < n4; j += U * 1024) {
+            f32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = x4[j + u * 1024];
+#pragma unroll
+            for (int u = 0; u < U; ++u) s += ((double)v[u][0] + (double)v[u][1]) + ((double)v[u][2] + (double)v[u][3]);
+        }
+        for (; j < n4; j += 1024) {
+            const f32x4 v = x4[j];
+            s += ((double)v[0] + (double)v[1]) + ((double)v[2] + (double)v[3]);
+        }
+        i0 = n4 * 4;
+    }
+    constexpr int U = 8;
+    int64_t i = i0 + threadIdx.x;
     for (; i + (U - 1) * 1024 < n; i += U * 1024) {
         float v[U];
 #pragma unroll
