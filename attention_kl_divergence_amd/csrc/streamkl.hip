@@ -327,6 +327,7 @@ __device__ inline f32x16 tile_scores(const char *tile, const u32x4 *xv, int l32,
 struct Online {
     float mt, lt, at, as;  // teacher: reference max of x_t, sum e_t, sum e_t x_t, sum e_t x_s
     float ms, ls;          // student: reference max of x_s, sum e_s
+    float nmt, nms;        // -c_t mt and -c_s ms, the exponent offsets of the references
 };
 
 // Exact update: the references become the running maxima and the sums are
@@ -357,6 +358,8 @@ __device__ inline void online_update(Online &o, f32x16 xt, f32x16 xs, float ct, 
     o.mt = mxt;
     o.ms = mxs;
     const float nmt = -ct * mxt, nms = -cs * mxs;
+    o.nmt = nmt;
+    o.nms = nms;
     float lt = 0.f, ls = 0.f, at = 0.f, as = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -384,7 +387,7 @@ __device__ inline void online_update(Online &o, f32x16 xt, f32x16 xs, float ct, 
 template <bool CAUSAL>
 __device__ inline void online_step(Online &o, const f32x16 &xt, const f32x16 &xs, float ct, float cs, int k0, int hf,
                                    int q, int n_k, int off) {
-    const float nmt = -ct * o.mt, nms = -cs * o.ms;
+    const float nmt = o.nmt, nms = o.nms;
     float lt = 0.f, ls = 0.f, at = 0.f, as = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -480,13 +483,19 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16FwdWaves : 1) void 
     load_span_global<T, DS>(Qs + (int64_t)qc * sqs, hf, qv, qsv);
 
     const float ct = p.tau_t * kLog2e, cs = p.tau_s * kLog2e;
-    Online o{kMasked, 0.f, 0.f, 0.f, kMasked, 0.f};
+    Online o{kMasked, 0.f, 0.f, 0.f, kMasked, 0.f, -ct * kMasked, -cs * kMasked};
 
     dma_barrier();
-    for (int it = 0; it < ntile; ++it) {
+    // one step per key tile.  Without a causal mask the loop runs two steps at
+    // a time, so that the ring stage SL = it % 2 is a compile-time offset and
+    // the LDS operand addresses need no per-tile arithmetic (measured slower
+    // for the causal kernels, which keep one step per iteration).
+    auto step = [&](int it, auto sl_tag) {
+        constexpr int SL = decltype(sl_tag)::value;
         // the other stage was read in the previous step: load tile it + 1 there
-        if (it + 1 < ntile) issue(it + 1, smem + ((it + 1) & 1) * STAGE);
-        const char *bc = smem + (it & 1) * STAGE;
+        const int sl = SL >= 0 ? SL : (it & 1);
+        if (it + 1 < ntile) issue(it + 1, smem + (sl ^ 1) * STAGE);
+        const char *bc = smem + sl * STAGE;
         if (active(it)) {
             const int k0 = (t0 + it) * kBN;
             const f32x16 xt = tile_scores<T, DT>(bc, qtv, l32, hf);
@@ -495,6 +504,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? kBf16FwdWaves : 1) void 
             else online_step<CAUSAL>(o, xt, xs, ct, cs, k0, hf, q, n_k, off);
         }
         dma_barrier();  // tile it + 1 is in LDS and every wave is done with tile it
+    };
+    if constexpr (CAUSAL) {
+        for (int it = 0; it < ntile; ++it) step(it, std::integral_constant<int, -1>{});
+    } else {
+        int it = 0;
+        for (; it + 1 < ntile; it += 2) {
+            step(it, std::integral_constant<int, 0>{});
+            step(it + 1, std::integral_constant<int, 1>{});
+        }
+        if (it < ntile) step(it, std::integral_constant<int, 0>{});
     }
 
     // merge the two half-waves (same query, disjoint key subsets)
