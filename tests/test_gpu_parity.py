@@ -204,6 +204,37 @@ def test_deterministic_bitwise():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("shift", [0, 1])
+@pytest.mark.parametrize("B,H,n_q", [(1, 3, 37), (1, 2, 20011)])
+def test_summed_kl_with_any_row_alignment(B, H, n_q, shift):
+    """The summed KL reads the per-row KLs 16 bytes at a time when they start on a
+    16-byte boundary and 4 bytes at a time otherwise (the ABI asks only for
+    contiguous fp32 rows).  Both give the fp64 sum of the rows the kernel wrote,
+    for row counts that leave a tail past the unrolled loop and the vectors, and
+    the rows themselves do not depend on where they are written."""
+    w = W["corr_4k"].resized(B=B, H=H, n_q=n_q, n_k=64, seed=212 + shift)
+    d = to_device(inputs.make(w), "bf16")
+    lib = skl.load_library()
+    rows = B * H * n_q
+    buf = torch.zeros(rows + 4, dtype=torch.float32, device="cuda")
+    kl = buf[shift:shift + rows]
+    assert (kl.data_ptr() % 16 == 0) == (shift == 0)
+    lt = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ls = torch.empty_like(lt)
+    tot = torch.zeros(1, dtype=torch.float32, device="cuda")
+    tau_t, tau_s = 1.0 / np.sqrt(w.d_t), 1.0 / np.sqrt(w.d_s)
+    code = lib.streamkl_fwd(d["q_t"].data_ptr(), d["k_t"].data_ptr(), d["q_s"].data_ptr(), d["k_s"].data_ptr(),
+                            skl._dtype_code(d["q_t"]), B, H, n_q, w.n_k, w.d_t, w.d_s, None, tau_t, tau_s, 0,
+                            kl.data_ptr(), lt.data_ptr(), ls.data_ptr(), tot.data_ptr(), skl._stream_ptr(d["q_t"].device))
+    assert code == 0
+    torch.cuda.synchronize()
+    k = kl.cpu().numpy()
+    ref = float(np.sum(k, dtype=np.float64))
+    assert abs(float(tot.item()) - ref) <= 1e-6 * float(np.sum(np.abs(k), dtype=np.float64)) + 1e-30
+    r = skl.streamkl_fwd(d["q_t"], d["k_t"], d["q_s"], d["k_s"])
+    assert torch.equal(r[0].reshape(-1), kl)
+
+
 def test_nan_query_row_is_confined():
     w = W["corr_4k"].resized(B=1, H=2, n_q=64, n_k=96, seed=211)
     x = inputs.make(w)
