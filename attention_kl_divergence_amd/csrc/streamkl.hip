@@ -39,6 +39,9 @@
 #include <type_traits>
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "streamkl.h"
 #include "streamkl_internal.h"
@@ -1421,6 +1424,14 @@ streamkl_status fwd_common(const void *q_t, const void *k_t, const void *q_s, co
     fwd_launch_t fn = dtype == STREAMKL_BF16 ? pick_fwd1<bf16_t>(d_t, d_s, causal) : pick_fwd1<float>(d_t, d_s, causal);
     if (!fn) return STREAMKL_ERR_UNSUPPORTED;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (streamkl_internal::log_enabled())
+        fprintf(stderr,
+                "[streamkl] fwd %s B=%d H=%d n_q=%d n_k=%d d_t=%d d_s=%d causal=%d: %d waves x %d query rows per "
+                "block, %d-key tiles, %d waves per SIMD; grid %d x %d threads; keys [%d, %d) in %d split(s) of %d; "
+                "%s order%s\n",
+                dtype == STREAMKL_BF16 ? "bf16" : "f32", B, H, n_q, n_k, d_t, d_s, causal, kWaves, kTile, kBN,
+                dtype == STREAMKL_BF16 ? kBf16FwdWaves : 1, B * H * p.n_qblk * n_split, kThreads, k_begin, k_end,
+                n_split, p.k_chunk, p.rank_major ? "rank-major" : "head-major", state ? ", raw states" : "");
     fn(p, B * H * p.n_qblk * n_split, hs);
     if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
     if (kl_sum && !state) {
@@ -1529,6 +1540,15 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
     };
     if (!grp) {
         pp[0].rank_major = pp[1].rank_major = order(true, true, (int64_t)B * H);
+        if (streamkl_internal::log_enabled())
+            fprintf(stderr,
+                    "[streamkl] bwd%s %s B=%d H=%d n_q=%d n_k=%d d_t=%d d_s=%d causal=%d: %d waves x %d rows per block, "
+                    "%d-row streamed tiles, %d per stage, %d waves per SIMD; grid %d x %d threads (%d query-major + "
+                    "%d key-major blocks per head), %s order, %s upstream gradient\n",
+                    first ? " (first argument)" : "", bf ? "bf16" : "f32", B, H, n_q, n_k, d_t, d_s, causal, kWaves,
+                    kTile, kBN, kBwdSub, bf ? kBf16Blocks * kWaves / 4 : 1, B * H * (pp[0].n_xblk + pp[1].n_xblk),
+                    kThreads, pp[0].n_xblk, pp[1].n_xblk, pp[0].rank_major ? "rank-major" : "head-major",
+                    gs ? "scalar" : "per-row");
         fn(pp[0], pp[1], B * H * (pp[0].n_xblk + pp[1].n_xblk), hs);
         if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
         return STREAMKL_OK;
@@ -1551,6 +1571,13 @@ streamkl_status bwd_common(const void *q_t, const void *k_t, const void *q_s, co
         none.n_xblk = 0;
         none.nheads = cur.nheads;
         cur.rank_major = none.rank_major = order(pass == 0, pass == 1, cur.nheads);
+        if (streamkl_internal::log_enabled())
+            fprintf(stderr,
+                    "[streamkl] bwd%s %s %s pass, grouped heads (%d KL heads per output head, %d split(s) of %d): "
+                    "grid %d x %d threads, %s order\n",
+                    first ? " (first argument)" : "", bf ? "bf16" : "f32", pass == 0 ? "query-major" : "key-major",
+                    cur.group, cur.nsplit, cur.hsplit, cur.nheads * cur.n_xblk, kThreads,
+                    cur.rank_major ? "rank-major" : "head-major");
         if (pass == 0) fn(cur, none, cur.nheads * cur.n_xblk, hs);
         else fn(none, cur, cur.nheads * cur.n_xblk, hs);
         if (hipGetLastError() != hipSuccess) return STREAMKL_ERR_HIP;
@@ -1801,6 +1828,14 @@ streamkl_status streamkl_bwd_teacher_ex(const void *q_t, const void *k_t, const 
 }  // extern "C"
 
 namespace streamkl_internal {
+bool log_enabled() {
+    static const bool on = [] {
+        const char *v = getenv("STREAMKL_LOG");
+        return v != nullptr && *v != '\0' && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
 hipError_t launch_row_sum(const float *x, int64_t n, float *out, hipStream_t s) {
     hipLaunchKernelGGL(streamkl_sum_kernel, dim3(1), dim3(1024), 0, s, x, n, out);
     return hipGetLastError();

@@ -13,6 +13,11 @@ namespace streamkl_internal {
 __attribute__((visibility("hidden"))) hipError_t launch_row_sum(const float *x, int64_t n, float *out,
                                                                 hipStream_t s);
 
+// True when the STREAMKL_LOG environment variable is set to anything but "0"
+// (read once per process): every launch then prints its configuration and
+// grid, one line on stderr.
+__attribute__((visibility("hidden"))) bool log_enabled();
+
 }  // namespace streamkl_internal
 
 #endif  // STREAMKL_INTERNAL_H

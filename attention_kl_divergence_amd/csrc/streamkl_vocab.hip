@@ -34,6 +34,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 
 #include "streamkl.h"
 #include "streamkl_internal.h"
@@ -624,6 +625,13 @@ streamkl_status vocab_launch(Mode mode, const void *z_t, const void *z_s, stream
                                                      : pick_vocab<float>(vec, dz_t != nullptr, wpr);
     const int rpb = wpr == 1 ? 4 : 1;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (streamkl_internal::log_enabled())
+        fprintf(stderr,
+                "[streamkl] vocab %s %s rows=%lld V=%d: %d wave(s) per row, %d row(s) per block, %s loads, "
+                "%lld launch(es) of up to %lld rows\n",
+                mode == kFwd ? "fwd" : (mode == kBwd ? "bwd" : "fused"), dtype == STREAMKL_BF16 ? "bf16" : "f32",
+                (long long)rows, V, wpr, rpb, vec ? "16-byte" : "element", (long long)((rows + kRowsPerLaunch - 1) / kRowsPerLaunch),
+                (long long)kRowsPerLaunch);
     for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
         const int64_t n = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
         VocabParams p{};
